@@ -1,0 +1,19 @@
+"""fp64 CPU oracle for one Medusa verification step.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the benchmark's CPU
+baseline, never by the HIP library or its Python binding.  It shares no code with them.
+
+Parts: heads + top-k (heads.py, C loops in medusa_oracle.c), the candidate tree (tree.py),
+tree-masked attention (attention.py, C loops) and typical acceptance (accept.py).  step.py
+chains them.
+"""
+
+from . import _clib  # noqa: F401
+from .accept import row_threshold, typical_accept  # noqa: F401
+from .attention import tree_attention  # noqa: F401
+from .heads import heads, project, topk, topk_ties  # noqa: F401
+from .tree import TreeError, build_static, canonical, gather  # noqa: F401
+
+
+def build():
+    _clib.build(force=True)
