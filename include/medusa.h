@@ -1,0 +1,225 @@
+/*
+ * medusa.h -- C ABI of libmedusa_hip.so: one Medusa verification step on an AMD MI355X
+ * (gfx950).
+ *
+ * The step, as the pages describe it:
+ *   1. medusa_heads    K heads read the last hidden state h; head k computes
+ *                      W2_k (h + SiLU(W1_k h + b1_k)) and keeps its top-k tokens.
+ *                      (Ultralytics glossary "Medusa Heads", section on how the heads predict
+ *                      the next tokens, and its code sample; Wiblog "Medusa multi-head
+ *                      speculative decoding", heads section and inference-flow section.)
+ *   2. build_tree      the heads' candidates are expanded into a fixed tree given by the
+ *                      `medusa_choices` list; its ancestor mask, parents and root-to-leaf paths
+ *                      are precomputed once, the per-step token ids and depth-based position
+ *                      ids are gathered on the device.  (Wiblog page, tree-attention section;
+ *                      Ultralytics page, tree-attention section; cnnetsun page, configuration
+ *                      section.)
+ *   3. tree_attention  every tree token attends to the prefix KV cache and to its own
+ *                      ancestors in the tree, never across branches.  (Wiblog page,
+ *                      tree-attention section; Ultralytics page, tree-attention section.)
+ *   4. typical_accept  a candidate is accepted when p(x) > min(eps, delta * exp(-H(p)));
+ *                      greedy (exact match) at temperature 0; the walk from the root stops at
+ *                      the first rejection or a leaf; the result is the best path and its
+ *                      accept length.  (Wiblog page, typical-acceptance and inference-flow
+ *                      sections; Ultralytics page, tree-attention section; cnnetsun page,
+ *                      architecture and candidate-filtering sections, which give the call
+ *                      evaluate_posterior(logits, candidates, temperature, posterior_threshold,
+ *                      posterior_alpha, ...) -> (best_candidate, accept_length) and the
+ *                      defaults 0.09 / 0.3.)
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device memory on the current device; "host" pointers are
+ *     ordinary host memory.  Every tensor is dense, row-major, 16-byte aligned.  The caller owns
+ *     every buffer, workspaces included; the library allocates no device memory and keeps no
+ *     state between calls except a thread-local error string.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All device work is enqueued on it
+ *     asynchronously; nothing synchronises the host except build_tree with static_ready == 0.
+ *   - dtype: MEDUSA_F32 (float) or MEDUSA_BF16 (bfloat16 bit patterns, uint16 storage).  It is
+ *     the element type of every floating-point tensor input of the call.
+ *   - Return value: MEDUSA_OK or a negative medusa_status.  Arguments are checked before any
+ *     launch: a call that fails validation writes nothing.  A fault of earlier asynchronous work
+ *     is reported as MEDUSA_ERR_HIP by the next call.  medusa_last_error() gives the text.
+ *   - Workspaces: size them with the matching *_workspace() query.  A workspace must be
+ *     zero-filled before its first use and not written by the caller afterwards (the kernels
+ *     leave their counters at zero when they finish).  Calls that share a workspace, or that run
+ *     concurrently on different streams with the same workspace, race.
+ */
+#ifndef MEDUSA_H
+#define MEDUSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;
+
+typedef enum {
+  MEDUSA_OK = 0,
+  MEDUSA_ERR_ARG = -1,         /* null pointer, bad scalar (temperature, eps, ...) */
+  MEDUSA_ERR_SHAPE = -2,       /* sizes out of the supported range */
+  MEDUSA_ERR_DTYPE = -3,       /* unknown dtype */
+  MEDUSA_ERR_TREE = -4,        /* malformed medusa_choices */
+  MEDUSA_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+  MEDUSA_ERR_HIP = -6,         /* HIP runtime error (launch failure or earlier async fault) */
+  MEDUSA_ERR_UNSUPPORTED = -7  /* valid request outside what this build implements */
+} medusa_status;
+
+/* Text describing the last failure on the calling thread ("" if none).  Never NULL. */
+const char* medusa_last_error(void);
+
+/* ---------------------------------------------------------------------------------------- *
+ * 1. Medusa heads + per-head top-k
+ * ---------------------------------------------------------------------------------------- */
+
+/* Workspace bytes for medusa_heads with these sizes (0 on invalid sizes). */
+size_t medusa_heads_workspace(int B, int hidden, long vocab, int K, int topk);
+
+/*
+ * For every sequence b < B and head k < K (Ultralytics "Medusa Heads", how-the-heads-predict
+ * section: one fully connected layer with SiLU and a residual connection, then a vocab
+ * projection; W1 has a bias, W2 has none; torch Linear [out, in] weight layout):
+ *     r[b,k]      = h[b] + SiLU(W1[k] h[b] + b1[k]),     SiLU(u) = u / (1 + e^-u)
+ *     logits[b,k] = W2[k] r[b,k]
+ *     topk_ids[b,k,0..topk-1] = the topk largest logits[b,k,:], descending; equal values go to
+ *                               the lower token id (Wiblog page, inference-flow section: each
+ *                               head outputs its top-k candidates).
+ * Arguments (all device):
+ *   h        [B, hidden]            dtype
+ *   w1       [K, hidden, hidden]    dtype  ([out, in])
+ *   b1       [K, hidden]            dtype
+ *   w2       [K, vocab, hidden]     dtype  ([out, in])
+ *   logits   [B, K, vocab] float32, or NULL (then kept in the workspace only)
+ *   topk_ids [B, K, topk] int32
+ *   topk_logits [B, K, topk] float32, or NULL
+ * Arithmetic: fp32 accumulation; r is kept in fp32.  For bf16 weights the fp32 r enters the
+ * matrix cores as a bf16 hi + lo pair (relative error about 2^-17 per element).
+ * Limits: 1 <= B <= 8, 32 <= hidden <= 16384 and hidden % 32 == 0, 1 <= vocab < 2^31,
+ *         1 <= K <= 8, 1 <= topk <= min(64, vocab).
+ */
+int medusa_heads(const void* h, const void* w1, const void* b1, const void* w2, int dtype, int B,
+                 int hidden, long vocab, int K, int topk, float* logits, int32_t* topk_ids,
+                 float* topk_logits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------- *
+ * 2. The candidate tree
+ * ---------------------------------------------------------------------------------------- */
+
+/*
+ * A tree given as `medusa_choices` (cnnetsun page, configuration section): n_choices rank
+ * tuples, choices[c*max_depth + d] for d < max_depth, padded with -1.  Tuple (r1..rd) is the
+ * node made of head 1's rank-r1 candidate, ..., head d's rank-rd candidate, so head d fills
+ * depth d; the root (depth 0) is the last accepted token.  The list must be prefix-closed
+ * (every proper prefix present), without duplicates, with every rank < topk and depth <= K.
+ *
+ * Node order: root = 0, then by (depth, rank tuple) ascending, so parent < child.
+ * Paths: one per leaf, leaves in ascending rank-tuple order.
+ */
+typedef struct {
+  int T;           /* nodes including the root */
+  int W;           /* 64-bit mask words per row: (T + 63) / 64 */
+  int n_paths;     /* root-to-leaf paths (leaves) */
+  int dmax;        /* tree depth */
+  int n_internal;  /* nodes with at least one child (the root included) */
+  /* device arrays, filled by build_tree(static_ready = 0) */
+  uint64_t* mask;      /* [T][W]: bit j%64 of word j/64 of row i is set iff node j is i or an
+                          ancestor of i (Wiblog page, tree-attention section: each token sees
+                          only its own prefix path) */
+  int32_t* parent;     /* [T], -1 for the root */
+  int32_t* depth;      /* [T] */
+  int32_t* rank;       /* [T], the node's last rank, -1 for the root */
+  int32_t* paths;      /* [n_paths][dmax + 1]: node per depth, -1 padded */
+  int32_t* path_len;   /* [n_paths]: depth of the leaf */
+  int32_t* child_ptr;  /* [T + 1]: children of i are child_idx[child_ptr[i] .. child_ptr[i+1]) */
+  int32_t* child_idx;  /* [T - 1] */
+  int32_t* internal;   /* [n_internal]: internal node ids, ascending */
+} medusa_tree;
+
+/*
+ * Host only.  Validates a choice list and fills T, W, n_paths, dmax and n_internal of *tree
+ * (its pointers are left untouched).  Returns MEDUSA_ERR_TREE for a malformed list.
+ * Limits: 1 <= n_choices, T <= 4096, 1 <= max_depth <= K <= 8, 1 <= topk <= 64.
+ */
+int medusa_tree_dims(const int32_t* choices, int n_choices, int max_depth, int K, int topk,
+                     medusa_tree* tree);
+
+/*
+ * The per-step tree tokens and position ids (Wiblog page, tree-attention section: the
+ * position encoding follows each token's path):
+ *     tokens[b][0] = root_tokens[b]
+ *     tokens[b][i] = topk_ids[b][depth(i) - 1][rank(i)]
+ *     position_ids[b][i] = prefix_len[b] + depth(i)
+ * static_ready == 0: the choice list (host) is validated, the static arrays of *tree are
+ *   computed on the host and copied into its device arrays (sized from medusa_tree_dims); the
+ *   host waits for that copy.  Do this once per tree; the pages precompute and cache the mask.
+ * static_ready == 1: the device arrays are taken as already filled; choices may be NULL.
+ * Arguments: topk_ids device [B][K][topk]; root_tokens, prefix_len device [B];
+ *            tokens, position_ids device [B][T] int32.
+ */
+int build_tree(const int32_t* choices, int n_choices, int max_depth, int K, int topk,
+               const int32_t* topk_ids, const int32_t* root_tokens, const int32_t* prefix_len,
+               int B, int static_ready, const medusa_tree* tree, int32_t* tokens,
+               int32_t* position_ids, void* stream);
+
+/* ---------------------------------------------------------------------------------------- *
+ * 3. Tree attention
+ * ---------------------------------------------------------------------------------------- */
+
+size_t tree_attention_workspace(int B, int Hq, int Hkv, int T, int D, int max_prefix_len);
+
+/*
+ * For every sequence b, query head hq and tree node i, with kv head g = hq / (Hq / Hkv):
+ *     visible rows j: every prefix row j < prefix_len[b], and row prefix_len[b] + t for every
+ *                     node t whose bit is set in mask row i (its ancestors and itself);
+ *     out[b,hq,i] = sum_j softmax_j(scale * q[b,hq,i] . k[b,g,j]) v[b,g,j]
+ * (Wiblog page, tree-attention section: one pass verifies all candidates; a token attends only
+ * to its own prefix path.)  The tree tokens' K/V must already sit at cache rows
+ * prefix_len[b] .. prefix_len[b] + T - 1, in node order.  No positional encoding is applied
+ * here: q and k arrive as the caller produced them.
+ * Arguments (device): q, out [B][Hq][T][D] dtype; k_cache, v_cache [B][Hkv][lcap][D] dtype;
+ *   prefix_len [B] int32 with prefix_len[b] <= max_prefix_len and prefix_len[b] + T <= lcap;
+ *   mask [T][W] uint64 as in medusa_tree.  scale <= 0 selects 1/sqrt(D).
+ * Arithmetic: fp32 scores, softmax and accumulation; bf16 operands enter the matrix cores
+ * directly; the output is rounded to dtype (nearest even).
+ * Limits: D in {64, 128}, Hq % Hkv == 0, 1 <= T <= 4096, 0 <= max_prefix_len <= 1<<20,
+ *         1 <= B, Hq <= 256.
+ */
+int tree_attention(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                   const int32_t* prefix_len, int max_prefix_len, long lcap,
+                   const uint64_t* mask, int B, int Hq, int Hkv, int T, int D, float scale,
+                   void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------- *
+ * 4. Typical acceptance
+ * ---------------------------------------------------------------------------------------- */
+
+size_t typical_accept_workspace(int B, int T, long vocab, int n_internal);
+
+/*
+ * logits [B][T][vocab] dtype (device): row n is the model's next-token distribution after tree
+ * node n, so child c of node n is judged by row n.  tokens [B][T] int32 (device) from
+ * build_tree.  For temperature > 0, per internal row n:
+ *     z = logits / temperature, p = softmax(z), H = -sum p ln p,
+ *     thr = min(posterior_threshold, posterior_alpha * exp(-H)),
+ *     child c accepted iff p(tokens[c]) > thr      (decided in fp32, in the log domain);
+ * for temperature == 0: child c accepted iff tokens[c] is the row's argmax (lowest id on ties).
+ * The root token is the greedy first token and is always kept.  Along each path the accept
+ * count is the number of accepted nodes below the root before the first rejection;
+ *     accept_length[b]  = the largest count,  best_candidate[b] = the lowest path index with it,
+ *     next_token[b]     = argmax of the row of the last accepted node of that path (NULL skips
+ *                         it), i.e. the greedy token that starts the next step.
+ * Leaf rows are read only for next_token.  Outputs are device int32 [B].
+ * Limits: temperature >= 0; 0 < posterior_threshold < 1; posterior_alpha > 0; vocab < 2^31.
+ */
+int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
+                   const int32_t* tokens, const medusa_tree* tree, float temperature,
+                   float posterior_threshold, float posterior_alpha, int32_t* best_candidate,
+                   int32_t* accept_length, int32_t* next_token, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MEDUSA_H */

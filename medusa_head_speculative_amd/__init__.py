@@ -1,0 +1,24 @@
+"""MI355X-native Medusa verification step: Python binding of libmedusa_hip.so.
+
+Entry points (same names as the C ABI in include/medusa.h): medusa_heads, build_tree,
+tree_attention, typical_accept, their *_workspace queries, the Tree helper (device arrays of a
+fixed tree) and VerifyStep (the four calls chained on one stream).
+"""
+
+from ._lib import (  # noqa: F401
+    BF16,
+    EXPORTS,
+    F32,
+    MedusaError,
+    Tree,
+    build_tree,
+    load,
+    medusa_heads,
+    medusa_heads_workspace,
+    tree_attention,
+    tree_attention_workspace,
+    typical_accept,
+    typical_accept_workspace,
+    workspace,
+)
+from .step import VerifyStep  # noqa: F401

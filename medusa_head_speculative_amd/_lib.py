@@ -1,0 +1,207 @@
+"""ctypes binding of libmedusa_hip.so.  Argument marshalling only: every step runs in HIP kernels.
+
+Tensors are torch tensors on the current HIP device (bf16 tensors may be torch.bfloat16 or
+int16/uint16 bit patterns); the functions pass their data pointers and the current stream to the
+C ABI declared in include/medusa.h and raise MedusaError on a non-zero status.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBPATH = os.path.join(HERE, "libmedusa_hip.so")
+
+F32, BF16 = 0, 1
+STATUS = {0: "OK", -1: "ERR_ARG", -2: "ERR_SHAPE", -3: "ERR_DTYPE", -4: "ERR_TREE",
+          -5: "ERR_WORKSPACE", -6: "ERR_HIP", -7: "ERR_UNSUPPORTED"}
+
+
+class MedusaError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class medusa_tree(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int), ("W", ctypes.c_int), ("n_paths", ctypes.c_int),
+                ("dmax", ctypes.c_int), ("n_internal", ctypes.c_int),
+                ("mask", ctypes.c_void_p), ("parent", ctypes.c_void_p),
+                ("depth", ctypes.c_void_p), ("rank", ctypes.c_void_p),
+                ("paths", ctypes.c_void_p), ("path_len", ctypes.c_void_p),
+                ("child_ptr", ctypes.c_void_p), ("child_idx", ctypes.c_void_p),
+                ("internal", ctypes.c_void_p)]
+
+
+EXPORTS = ["medusa_last_error", "medusa_heads_workspace", "medusa_heads", "medusa_tree_dims",
+           "build_tree", "tree_attention_workspace", "tree_attention",
+           "typical_accept_workspace", "typical_accept"]
+
+_lib = None
+
+
+def load():
+    """Load libmedusa_hip.so (raises if it has not been built: there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBPATH):
+        raise ImportError(f"{LIBPATH} is missing: build it with "
+                          "`python -m medusa_head_speculative_amd.build`")
+    L = ctypes.CDLL(LIBPATH)
+    vp, i, l, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_float, ctypes.c_size_t
+    tp = ctypes.POINTER(medusa_tree)
+    L.medusa_last_error.restype = ctypes.c_char_p
+    L.medusa_last_error.argtypes = []
+    L.medusa_heads_workspace.restype = sz
+    L.medusa_heads_workspace.argtypes = [i, i, l, i, i]
+    L.medusa_heads.restype = i
+    L.medusa_heads.argtypes = [vp, vp, vp, vp, i, i, i, l, i, i, vp, vp, vp, vp, sz, vp]
+    L.medusa_tree_dims.restype = i
+    L.medusa_tree_dims.argtypes = [vp, i, i, i, i, tp]
+    L.build_tree.restype = i
+    L.build_tree.argtypes = [vp, i, i, i, i, vp, vp, vp, i, i, tp, vp, vp, vp]
+    L.tree_attention_workspace.restype = sz
+    L.tree_attention_workspace.argtypes = [i, i, i, i, i, i]
+    L.tree_attention.restype = i
+    L.tree_attention.argtypes = [vp, vp, vp, i, vp, i, l, vp, i, i, i, i, i, f, vp, vp, sz, vp]
+    L.typical_accept_workspace.restype = sz
+    L.typical_accept_workspace.argtypes = [i, i, l, i]
+    L.typical_accept.restype = i
+    L.typical_accept.argtypes = [vp, i, i, i, l, vp, tp, f, f, f, vp, vp, vp, vp, sz, vp]
+    _lib = L
+    return L
+
+
+def _check(rc):
+    if rc != 0:
+        raise MedusaError(rc, load().medusa_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def workspace(nbytes, device=None):
+    """A zero-filled workspace (the kernels keep their counters at zero between calls)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+
+
+# ---------------------------------------------------------------------------------------------
+def medusa_heads_workspace(B, hidden, vocab, K, topk):
+    return load().medusa_heads_workspace(B, hidden, vocab, K, topk)
+
+
+def medusa_heads(h, w1, b1, w2, topk, topk_ids, ws, logits=None, topk_logits=None, stream=None):
+    """h [B,Hd]; w1 [K,Hd,Hd]; b1 [K,Hd]; w2 [K,V,Hd]; topk_ids [B,K,topk] int32 (out)."""
+    B, hd = h.shape
+    K, V = w2.shape[0], w2.shape[1]
+    _check(load().medusa_heads(_ptr(h), _ptr(w1), _ptr(b1), _ptr(w2), dtype_code(h), B, hd, V, K,
+                               topk, _ptr(logits), _ptr(topk_ids), _ptr(topk_logits), _ptr(ws),
+                               ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------------------------
+def _choices_array(choices, max_depth=None):
+    import numpy as np
+    md = max_depth or max(len(c) for c in choices)
+    a = np.full((len(choices), md), -1, np.int32)
+    for r, c in enumerate(choices):
+        a[r, :len(c)] = c
+    return a, md
+
+
+class Tree:
+    """Device arrays of one fixed tree (medusa_tree) plus its dims.  Built once per tree."""
+
+    def __init__(self, choices, K, topk, device="cuda"):
+        L = load()
+        self.choices, self.max_depth = _choices_array(choices)
+        self.K, self.topk = K, topk
+        self.c = medusa_tree()
+        _check(L.medusa_tree_dims(ctypes.c_void_p(self.choices.ctypes.data), len(choices),
+                                  self.max_depth, K, topk, ctypes.byref(self.c)))
+        T, W, P, dm, ni = self.c.T, self.c.W, self.c.n_paths, self.c.dmax, self.c.n_internal
+        i32 = dict(dtype=torch.int32, device=device)
+        self.mask = torch.zeros((T, W), dtype=torch.int64, device=device)
+        self.parent = torch.zeros(T, **i32)
+        self.depth = torch.zeros(T, **i32)
+        self.rank = torch.zeros(T, **i32)
+        self.paths = torch.zeros((P, dm + 1), **i32)
+        self.path_len = torch.zeros(P, **i32)
+        self.child_ptr = torch.zeros(T + 1, **i32)
+        self.child_idx = torch.zeros(max(T - 1, 1), **i32)
+        self.internal = torch.zeros(ni, **i32)
+        for name in ("mask", "parent", "depth", "rank", "paths", "path_len", "child_ptr",
+                     "child_idx", "internal"):
+            setattr(self.c, name, getattr(self, name).data_ptr())
+        self.static_ready = 0
+
+    @property
+    def T(self):
+        return self.c.T
+
+    @property
+    def dims(self):
+        c = self.c
+        return dict(T=c.T, W=c.W, n_paths=c.n_paths, dmax=c.dmax, n_internal=c.n_internal)
+
+
+def build_tree(tree, topk_ids, root_tokens, prefix_len, tokens, position_ids, stream=None):
+    """First call uploads the static arrays (host waits); later calls only gather."""
+    B = root_tokens.shape[0]
+    _check(load().build_tree(ctypes.c_void_p(tree.choices.ctypes.data), tree.choices.shape[0],
+                             tree.max_depth, tree.K, tree.topk, _ptr(topk_ids), _ptr(root_tokens),
+                             _ptr(prefix_len), B, tree.static_ready, ctypes.byref(tree.c),
+                             _ptr(tokens), _ptr(position_ids), _stream(stream)))
+    tree.static_ready = 1
+
+
+# ---------------------------------------------------------------------------------------------
+def tree_attention_workspace(B, Hq, Hkv, T, D, max_prefix_len):
+    return load().tree_attention_workspace(B, Hq, Hkv, T, D, max_prefix_len)
+
+
+def tree_attention(q, k_cache, v_cache, prefix_len, max_prefix_len, mask, out, ws, scale=0.0,
+                   stream=None):
+    """q/out [B,Hq,T,D]; caches [B,Hkv,Lcap,D]; mask [T,W] int64 bit words."""
+    B, Hq, T, D = q.shape
+    Hkv, lcap = k_cache.shape[1], k_cache.shape[2]
+    _check(load().tree_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), dtype_code(q),
+                                 _ptr(prefix_len), max_prefix_len, lcap, _ptr(mask), B, Hq, Hkv, T,
+                                 D, scale, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------------------------
+def typical_accept_workspace(B, T, V, n_internal):
+    return load().typical_accept_workspace(B, T, V, n_internal)
+
+
+def typical_accept(logits, tokens, tree, temperature, posterior_threshold, posterior_alpha,
+                   best_candidate, accept_length, ws, next_token=None, stream=None):
+    """logits [B,T,V]; tokens [B,T] int32; outputs int32 [B]."""
+    B, T, V = logits.shape
+    _check(load().typical_accept(_ptr(logits), dtype_code(logits), B, T, V, _ptr(tokens),
+                                 ctypes.byref(tree.c), temperature, posterior_threshold,
+                                 posterior_alpha, _ptr(best_candidate), _ptr(accept_length),
+                                 _ptr(next_token), _ptr(ws), ws.numel(), _stream(stream)))

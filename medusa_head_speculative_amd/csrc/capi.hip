@@ -1,0 +1,309 @@
+// C ABI of libmedusa_hip: argument validation, error reporting, workspace sizing, the host-side
+// static tree, and dispatch to the kernel launchers.  Every check runs before any launch, so a
+// rejected call writes nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <vector>
+
+#include "../../include/medusa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+// A fault of earlier asynchronous work (or a failed launch) is reported by the next call.
+int check_pending() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MEDUSA_ERR_HIP, "HIP error from earlier work: %s", hipGetErrorString(e));
+  return MEDUSA_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MEDUSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return MEDUSA_OK;
+}
+
+bool dtype_ok(int dt) { return dt == MEDUSA_F32 || dt == MEDUSA_BF16; }
+
+// ---- static tree (host) -------------------------------------------------------------------
+struct HostTree {
+  int T = 0, W = 0, P = 0, dmax = 0, n_int = 0;
+  std::vector<uint64_t> mask;
+  std::vector<int32_t> parent, depth, rank, paths, path_len, child_ptr, child_idx, internal;
+};
+
+int parse_tree(const int32_t* choices, int n, int max_depth, int K, int topk, HostTree* out,
+               bool want_arrays) {
+  if (!choices) return fail(MEDUSA_ERR_ARG, "choices is NULL");
+  if (n < 1 || n > 4095) return fail(MEDUSA_ERR_TREE, "n_choices = %d, need 1..4095", n);
+  if (max_depth < 1 || max_depth > 8) return fail(MEDUSA_ERR_TREE, "max_depth = %d, need 1..8", max_depth);
+  if (K < 1 || K > 8) return fail(MEDUSA_ERR_SHAPE, "K = %d, need 1..8", K);
+  if (topk < 1 || topk > 64) return fail(MEDUSA_ERR_SHAPE, "topk = %d, need 1..64", topk);
+  std::vector<std::vector<int32_t>> tup(n);
+  for (int c = 0; c < n; ++c) {
+    int d = 0;
+    while (d < max_depth && choices[c * max_depth + d] >= 0) ++d;
+    for (int e = d; e < max_depth; ++e)
+      if (choices[c * max_depth + e] != -1)
+        return fail(MEDUSA_ERR_TREE, "choice %d: entries after the first -1 must be -1", c);
+    if (d == 0) return fail(MEDUSA_ERR_TREE, "choice %d is empty", c);
+    if (d > K) return fail(MEDUSA_ERR_TREE, "choice %d has depth %d > K = %d", c, d, K);
+    for (int e = 0; e < d; ++e)
+      if (choices[c * max_depth + e] >= topk)
+        return fail(MEDUSA_ERR_TREE, "choice %d: rank %d >= topk = %d", c, choices[c * max_depth + e], topk);
+    tup[c].assign(choices + c * max_depth, choices + c * max_depth + d);
+  }
+  std::sort(tup.begin(), tup.end(), [](const std::vector<int32_t>& a, const std::vector<int32_t>& b) {
+    return a.size() != b.size() ? a.size() < b.size() : a < b;
+  });
+  for (int c = 1; c < n; ++c)
+    if (tup[c] == tup[c - 1]) return fail(MEDUSA_ERR_TREE, "duplicate choice");
+  std::map<std::vector<int32_t>, int> index;
+  index[{}] = 0;
+  for (int c = 0; c < n; ++c) index[tup[c]] = c + 1;
+  const int T = n + 1;
+  std::vector<int32_t> parent(T, -1), depth(T, 0), rank(T, -1);
+  for (int c = 0; c < n; ++c) {
+    std::vector<int32_t> pre(tup[c].begin(), tup[c].end() - 1);
+    auto it = index.find(pre);
+    if (it == index.end()) return fail(MEDUSA_ERR_TREE, "choice list is not prefix-closed");
+    parent[c + 1] = it->second;
+    depth[c + 1] = static_cast<int32_t>(tup[c].size());
+    rank[c + 1] = tup[c].back();
+  }
+  std::vector<int32_t> nchild(T, 0);
+  for (int i = 1; i < T; ++i) ++nchild[parent[i]];
+  HostTree& h = *out;
+  h.T = T;
+  h.W = (T + 63) / 64;
+  h.dmax = *std::max_element(depth.begin(), depth.end());
+  h.P = 0;
+  h.n_int = 0;
+  for (int i = 0; i < T; ++i) (nchild[i] == 0 ? h.P : h.n_int) += 1;
+  if (!want_arrays) return MEDUSA_OK;
+  h.parent = parent;
+  h.depth = depth;
+  h.rank = rank;
+  h.mask.assign(static_cast<size_t>(T) * h.W, 0ull);
+  for (int i = 0; i < T; ++i)
+    for (int j = i; j >= 0; j = parent[j]) h.mask[static_cast<size_t>(i) * h.W + j / 64] |= 1ull << (j % 64);
+  h.child_ptr.assign(T + 1, 0);
+  for (int i = 0; i < T; ++i) h.child_ptr[i + 1] = h.child_ptr[i] + nchild[i];
+  h.child_idx.assign(std::max(T - 1, 1), 0);
+  std::vector<int32_t> fill(h.child_ptr.begin(), h.child_ptr.end() - 1);
+  for (int i = 1; i < T; ++i) h.child_idx[fill[parent[i]]++] = i;   // ascending node order
+  for (int i = 0; i < T; ++i)
+    if (nchild[i]) h.internal.push_back(i);
+  // leaves in rank-tuple order: node order is (depth, tuple); sort leaves by tuple
+  std::vector<int> leaves;
+  for (int i = 1; i < T; ++i)
+    if (!nchild[i]) leaves.push_back(i);
+  std::sort(leaves.begin(), leaves.end(), [&](int a, int b) { return tup[a - 1] < tup[b - 1]; });
+  h.paths.assign(static_cast<size_t>(h.P) * (h.dmax + 1), -1);
+  h.path_len.assign(h.P, 0);
+  for (int p = 0; p < h.P; ++p) {
+    int d = depth[leaves[p]];
+    h.path_len[p] = d;
+    for (int j = leaves[p]; j >= 0; j = parent[j]) h.paths[static_cast<size_t>(p) * (h.dmax + 1) + depth[j]] = j;
+  }
+  return MEDUSA_OK;
+}
+
+template <typename T>
+int upload(T* dst, const std::vector<T>& src, const char* name) {
+  if (!dst) return fail(MEDUSA_ERR_ARG, "tree->%s is NULL", name);
+  hipError_t e = hipMemcpy(dst, src.data(), sizeof(T) * src.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(MEDUSA_ERR_HIP, "copy of tree->%s: %s", name, hipGetErrorString(e));
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* medusa_last_error(void) { return g_err; }
+
+// ---- heads ----------------------------------------------------------------------------------
+static int heads_shape(int B, int hidden, long vocab, int K, int topk) {
+  if (B < 1 || B > 8) return fail(MEDUSA_ERR_SHAPE, "B = %d, need 1..8", B);
+  if (hidden < 32 || hidden > 16384 || hidden % 32)
+    return fail(MEDUSA_ERR_SHAPE, "hidden = %d, need a multiple of 32 in 32..16384", hidden);
+  if (vocab < 1 || vocab >= (1l << 31)) return fail(MEDUSA_ERR_SHAPE, "vocab = %ld out of range", vocab);
+  if (K < 1 || K > 8) return fail(MEDUSA_ERR_SHAPE, "K = %d, need 1..8", K);
+  if (topk < 1 || topk > 64 || topk > vocab) return fail(MEDUSA_ERR_SHAPE, "topk = %d, need 1..min(64, vocab)", topk);
+  return MEDUSA_OK;
+}
+
+size_t medusa_heads_workspace(int B, int hidden, long vocab, int K, int topk) {
+  if (heads_shape(B, hidden, vocab, K, topk) != MEDUSA_OK) return 0;
+  return medusa::heads_ws_layout(B, hidden, vocab, K, topk).total;
+}
+
+int medusa_heads(const void* h, const void* w1, const void* b1, const void* w2, int dtype, int B,
+                 int hidden, long vocab, int K, int topk, float* logits, int32_t* topk_ids,
+                 float* topk_logits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_DTYPE, "dtype = %d", dtype);
+  if (!h || !w1 || !b1 || !w2 || !topk_ids) return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
+  int rc = heads_shape(B, hidden, vocab, K, topk);
+  if (rc) return rc;
+  const size_t need = medusa::heads_ws_layout(B, hidden, vocab, K, topk).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if ((rc = check_pending())) return rc;
+  return launched(medusa::launch_heads(h, w1, b1, w2, dtype, B, hidden, vocab, K, topk, logits,
+                                       topk_ids, topk_logits, static_cast<char*>(workspace),
+                                       static_cast<hipStream_t>(stream)),
+                  "medusa_heads");
+}
+
+// ---- tree -----------------------------------------------------------------------------------
+int medusa_tree_dims(const int32_t* choices, int n_choices, int max_depth, int K, int topk,
+                     medusa_tree* tree) {
+  if (!tree) return fail(MEDUSA_ERR_ARG, "tree is NULL");
+  HostTree h;
+  int rc = parse_tree(choices, n_choices, max_depth, K, topk, &h, false);
+  if (rc) return rc;
+  tree->T = h.T;
+  tree->W = h.W;
+  tree->n_paths = h.P;
+  tree->dmax = h.dmax;
+  tree->n_internal = h.n_int;
+  g_err[0] = '\0';
+  return MEDUSA_OK;
+}
+
+int build_tree(const int32_t* choices, int n_choices, int max_depth, int K, int topk,
+               const int32_t* topk_ids, const int32_t* root_tokens, const int32_t* prefix_len,
+               int B, int static_ready, const medusa_tree* tree, int32_t* tokens,
+               int32_t* position_ids, void* stream) {
+  if (!tree) return fail(MEDUSA_ERR_ARG, "tree is NULL");
+  if (!topk_ids || !root_tokens || !prefix_len || !tokens || !position_ids)
+    return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
+  if (B < 1 || B > 4096) return fail(MEDUSA_ERR_SHAPE, "B = %d", B);
+  if (K < 1 || K > 8 || topk < 1 || topk > 64) return fail(MEDUSA_ERR_SHAPE, "K = %d, topk = %d", K, topk);
+  if (static_ready != 0 && static_ready != 1) return fail(MEDUSA_ERR_ARG, "static_ready must be 0 or 1");
+  if (!tree->depth || !tree->rank) return fail(MEDUSA_ERR_ARG, "tree->depth / tree->rank is NULL");
+  int rc;
+  if (static_ready == 0) {
+    HostTree h;
+    if ((rc = parse_tree(choices, n_choices, max_depth, K, topk, &h, true))) return rc;
+    if (tree->T != h.T || tree->W != h.W || tree->n_paths != h.P || tree->dmax != h.dmax ||
+        tree->n_internal != h.n_int)
+      return fail(MEDUSA_ERR_TREE, "tree dims do not match the choice list (call medusa_tree_dims)");
+    if ((rc = check_pending())) return rc;
+    if ((rc = upload(tree->mask, h.mask, "mask")) || (rc = upload(tree->parent, h.parent, "parent")) ||
+        (rc = upload(tree->depth, h.depth, "depth")) || (rc = upload(tree->rank, h.rank, "rank")) ||
+        (rc = upload(tree->paths, h.paths, "paths")) ||
+        (rc = upload(tree->path_len, h.path_len, "path_len")) ||
+        (rc = upload(tree->child_ptr, h.child_ptr, "child_ptr")) ||
+        (rc = upload(tree->child_idx, h.child_idx, "child_idx")) ||
+        (rc = upload(tree->internal, h.internal, "internal")))
+      return rc;
+  } else {
+    if (tree->T < 2 || tree->T > 4096) return fail(MEDUSA_ERR_TREE, "tree->T = %d", tree->T);
+    if ((rc = check_pending())) return rc;
+  }
+  return launched(medusa::launch_tree_gather(topk_ids, K, topk, root_tokens, prefix_len, B, tree->T,
+                                             tree->depth, tree->rank, tokens, position_ids,
+                                             static_cast<hipStream_t>(stream)),
+                  "build_tree");
+}
+
+// ---- tree attention -------------------------------------------------------------------------
+static int attn_shape(int B, int Hq, int Hkv, int T, int D, int max_prefix_len) {
+  if (B < 1 || Hq < 1 || Hq > 256 || Hkv < 1 || Hq % Hkv)
+    return fail(MEDUSA_ERR_SHAPE, "B = %d, Hq = %d, Hkv = %d (need Hq %% Hkv == 0, Hq <= 256)", B, Hq, Hkv);
+  if (D != 64 && D != 128) return fail(MEDUSA_ERR_SHAPE, "D = %d, need 64 or 128", D);
+  if (T < 1 || T > 4096) return fail(MEDUSA_ERR_SHAPE, "T = %d, need 1..4096", T);
+  if (max_prefix_len < 0 || max_prefix_len > (1 << 20)) return fail(MEDUSA_ERR_SHAPE, "max_prefix_len = %d", max_prefix_len);
+  return MEDUSA_OK;
+}
+
+size_t tree_attention_workspace(int B, int Hq, int Hkv, int T, int D, int max_prefix_len) {
+  if (attn_shape(B, Hq, Hkv, T, D, max_prefix_len) != MEDUSA_OK) return 0;
+  // the larger of the two dtype plans, so one query serves both
+  size_t a = medusa::attn_plan(1, B, Hq, Hkv, T, D, max_prefix_len).total;
+  return a < 256 ? 256 : a;
+}
+
+int tree_attention(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                   const int32_t* prefix_len, int max_prefix_len, long lcap,
+                   const uint64_t* mask, int B, int Hq, int Hkv, int T, int D, float scale,
+                   void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_DTYPE, "dtype = %d", dtype);
+  if (!q || !k_cache || !v_cache || !prefix_len || !mask || !out)
+    return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
+  int rc = attn_shape(B, Hq, Hkv, T, D, max_prefix_len);
+  if (rc) return rc;
+  if (lcap < static_cast<long>(max_prefix_len) + T) return fail(MEDUSA_ERR_SHAPE, "lcap = %ld < max_prefix_len + T", lcap);
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(static_cast<float>(D));
+  if (!std::isfinite(scale)) return fail(MEDUSA_ERR_ARG, "scale is not finite");
+  const size_t need = medusa::attn_plan(dtype, B, Hq, Hkv, T, D, max_prefix_len).total;
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if ((rc = check_pending())) return rc;
+  return launched(medusa::launch_tree_attention(q, k_cache, v_cache, dtype, prefix_len, max_prefix_len,
+                                                lcap, mask, B, Hq, Hkv, T, D, scale, out,
+                                                static_cast<char*>(workspace),
+                                                static_cast<hipStream_t>(stream)),
+                  "tree_attention");
+}
+
+// ---- typical acceptance ---------------------------------------------------------------------
+size_t typical_accept_workspace(int B, int T, long vocab, int n_internal) {
+  if (B < 1 || T < 2 || T > 4096 || vocab < 1 || vocab >= (1l << 31) || n_internal < 1 || n_internal >= T) return 0;
+  return medusa::accept_ws_layout(B, T, vocab, n_internal).total;
+}
+
+int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
+                   const int32_t* tokens, const medusa_tree* tree, float temperature,
+                   float posterior_threshold, float posterior_alpha, int32_t* best_candidate,
+                   int32_t* accept_length, int32_t* next_token, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_DTYPE, "dtype = %d", dtype);
+  if (!logits || !tokens || !tree || !best_candidate || !accept_length)
+    return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
+  if (!tree->internal || !tree->child_ptr || !tree->child_idx || !tree->paths || !tree->path_len)
+    return fail(MEDUSA_ERR_ARG, "a tree array is NULL");
+  if (B < 1 || B > 65535) return fail(MEDUSA_ERR_SHAPE, "B = %d", B);
+  if (T != tree->T || T < 2 || T > 4096) return fail(MEDUSA_ERR_SHAPE, "T = %d does not match tree->T = %d", T, tree->T);
+  if (vocab < 1 || vocab >= (1l << 31)) return fail(MEDUSA_ERR_SHAPE, "vocab = %ld", vocab);
+  if (tree->n_internal < 1 || tree->n_internal >= T || tree->n_paths < 1 || tree->dmax < 1)
+    return fail(MEDUSA_ERR_TREE, "tree dims are inconsistent");
+  if (!(temperature >= 0.f) || !std::isfinite(temperature)) return fail(MEDUSA_ERR_ARG, "temperature = %g, need >= 0", temperature);
+  if (!(posterior_threshold > 0.f && posterior_threshold < 1.f))
+    return fail(MEDUSA_ERR_ARG, "posterior_threshold = %g, need 0 < eps < 1", posterior_threshold);
+  if (!(posterior_alpha > 0.f) || !std::isfinite(posterior_alpha))
+    return fail(MEDUSA_ERR_ARG, "posterior_alpha = %g, need > 0", posterior_alpha);
+  const size_t need = medusa::accept_ws_layout(B, T, vocab, tree->n_internal).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  int rc;
+  if ((rc = check_pending())) return rc;
+  return launched(medusa::launch_typical_accept(logits, dtype, B, T, vocab, tokens, tree->n_internal,
+                                                tree->internal, tree->child_ptr, tree->child_idx,
+                                                tree->paths, tree->path_len, tree->n_paths, tree->dmax,
+                                                temperature, posterior_threshold, posterior_alpha,
+                                                best_candidate, accept_length, next_token,
+                                                static_cast<char*>(workspace),
+                                                static_cast<hipStream_t>(stream)),
+                  "typical_accept");
+}
+
+}  // extern "C"

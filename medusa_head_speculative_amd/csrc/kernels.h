@@ -1,0 +1,54 @@
+// Internal launchers of libmedusa_hip (host side).  Arguments are validated by the C ABI layer
+// before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace medusa {
+
+// ---- heads -------------------------------------------------------------------------------
+struct HeadsWs {
+  size_t r, xfrag, logits, part, counters, total;
+  int chunks;
+};
+HeadsWs heads_ws_layout(int B, int hd, long V, int K, int topk);
+hipError_t launch_heads(const void* h, const void* w1, const void* b1, const void* w2, int dtype,
+                        int B, int hd, long V, int K, int topk, float* logits, int32_t* topk_ids,
+                        float* topk_logits, char* ws, hipStream_t s);
+
+// ---- tree --------------------------------------------------------------------------------
+hipError_t launch_tree_gather(const int32_t* topk_ids, int K, int topk, const int32_t* root_tokens,
+                              const int32_t* prefix_len, int B, int T, const int32_t* depth,
+                              const int32_t* rank, int32_t* tokens, int32_t* position_ids,
+                              hipStream_t s);
+
+// ---- tree attention ----------------------------------------------------------------------
+struct AttnPlan {
+  int G;          // q heads per kv head
+  int M;          // query rows per (b, kv head) = G * T
+  int qtiles;     // work-group query tiles per (b, kv head)
+  int splits;     // KV splits per (b, kv head, q tile)
+  size_t ws_o, ws_ml, ws_cnt, total;
+};
+AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_prefix_len);
+hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, int dtype,
+                                 const int32_t* prefix_len, int max_prefix_len, long lcap,
+                                 const uint64_t* mask, int B, int Hq, int Hkv, int T, int D,
+                                 float scale, void* out, char* ws, hipStream_t s);
+
+// ---- typical acceptance ------------------------------------------------------------------
+struct AcceptWs {
+  size_t part, dec, cnt_row, cnt_b, last, npart, cnt_nt, total;
+  int chunks;
+};
+AcceptWs accept_ws_layout(int B, int T, long V, int n_internal);
+hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, long V,
+                                 const int32_t* tokens, int n_internal, const int32_t* internal,
+                                 const int32_t* child_ptr, const int32_t* child_idx,
+                                 const int32_t* paths, const int32_t* path_len, int n_paths,
+                                 int dmax, float temperature, float eps, float delta,
+                                 int32_t* best, int32_t* accept_len, int32_t* next_token,
+                                 char* ws, hipStream_t s);
+
+}  // namespace medusa

@@ -1,0 +1,440 @@
+// Tree-masked attention of the candidate tokens over the prefix KV cache and their ancestors.
+//
+// Wiblog "Medusa multi-head speculative decoding", tree-attention section: all candidates are
+// verified in one forward pass; a token attends only to the tokens on its own prefix path,
+// never across branches; the fixed tree's mask is precomputed.  Ultralytics "Medusa Heads",
+// tree-attention section: each token sees only its ancestors in the tree.
+//
+// bf16 path (matrix cores).  A work-group owns 128 query rows of one (sequence, kv head): the
+// rows are (node, q head of the group) pairs, node-major, so grouped query heads share every
+// K/V tile.  It walks 64-row K/V tiles (the prefix, then the tree rows), staged in LDS row-major:
+//   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q rows held in registers;
+//                 a lane ends up with 4 columns of one query row per 16-column block, so the
+//                 online softmax runs per lane plus two cross-lane steps;
+//   O^T = V^T P^T the exponentiated scores are already laid out as the B operand; the A operand
+//                 V^T comes from LDS with ds_read_b64_tr_b16 (16-lane transposed reads), so V is
+//                 never transposed in memory.
+// Tree tiles that no row of the work-group can see are skipped; inside a tile each row's mask
+// word selects its ancestors.  When there are too few (sequence, kv head, query tile) units to
+// fill the chip, the K/V range is split and a second kernel merges the partial results in a
+// fixed order.  fp32 path (small models): one wave per output row, plain FMAs.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace medusa {
+
+constexpr int kAttnRows = 128;   // query rows per work-group (4 waves x 32)
+constexpr int kKvTile = 64;
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* prefix_len;
+  const uint64_t* mask;
+  uint16_t* out;
+  float* o_part;     // [splits][B][Hkv][Mpad][D]
+  float2* ml_part;   // [splits][B][Hkv][Mpad]
+  long lcap;
+  int B, Hq, Hkv, T, W, G, M, Mpad, qtiles, splits, nwork, Lmax;
+  float sl2;         // scale * log2(e)
+};
+
+__device__ __forceinline__ bf16x8_t lds_read16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ s16x4_t lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_rne(lo)) | (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
+  constexpr int KP = D + 8;              // LDS row pitch in elements (272 B for D = 128)
+  constexpr int NKB = D / 32;            // 32-wide contraction blocks over the head dim
+  constexpr int NDB = D / 16;            // 16-wide output blocks over the head dim
+  constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
+  constexpr int CPT = kKvTile * CPR / 256;  // chunks per thread per tile
+  __shared__ __align__(16) uint16_t Ks[kKvTile * KP];
+  __shared__ __align__(16) uint16_t Vs[kKvTile * KP];
+  __shared__ int s_active[64];
+
+  // ---- work item; consecutive logical items (query tiles of one K/V range) share an XCD ----
+  const int per_xcd = gridDim.x >> 3;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (logical >= a.nwork) return;
+  const int qt = logical % a.qtiles;
+  int rest = logical / a.qtiles;
+  const int split = rest % a.splits;
+  rest /= a.splits;
+  const int kvh = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, mm = lane & 15;
+  const int L = min(max(a.prefix_len[b], 0), a.Lmax);   // callers promise prefix_len <= Lmax
+  const int np = (L + kKvTile - 1) / kKvTile;
+  const int ntt = (a.T + kKvTile - 1) / kKvTile;
+  const int ntiles = np + ntt;
+  const int t_begin = static_cast<int>((static_cast<long>(split) * ntiles) / a.splits);
+  const int t_end = static_cast<int>((static_cast<long>(split + 1) * ntiles) / a.splits);
+  const long kvbase = (static_cast<long>(b) * a.Hkv + kvh) * a.lcap;
+
+  // ---- tree tiles that some row of this work-group can see ----
+  for (int t = tid; t < 64; t += 256) s_active[t] = 0;
+  __syncthreads();
+  for (int p = tid; p < kAttnRows * ntt; p += 256) {
+    const int r = p / ntt, t = p - r * ntt;
+    const int m = qt * kAttnRows + r;
+    if (m < a.M && a.mask[static_cast<long>(m / a.G) * a.W + t] != 0ull) s_active[t] = 1;
+  }
+  __syncthreads();
+
+  // ---- this lane's two query rows (mb = 0, 1) ----
+  int node[2];
+  bool rvalid[2];
+  bf16x8_t qf[2][NKB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = qt * kAttnRows + wave * 32 + mb * 16 + mm;
+    rvalid[mb] = m < a.M;
+    node[mb] = rvalid[mb] ? m / a.G : 0;
+    const int hq = kvh * a.G + (rvalid[mb] ? m % a.G : 0);
+    const uint16_t* qrow = a.q + ((static_cast<long>(b) * a.Hq + hq) * a.T + node[mb]) * D;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      qf[mb][kb] = rvalid[mb] ? load_bf16x8(qrow + kb * 32 + 8 * lg) : zero_bf16x8();
+  }
+
+  float mrow[2] = {-INFINITY, -INFINITY};
+  float lsum[2] = {0.f, 0.f};
+  f32x4_t oacc[2][NDB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto next_active = [&](int t) {
+    while (t < t_end && t >= np && !s_active[t - np]) ++t;
+    return t;
+  };
+  // first cache row and number of valid rows of tile t
+  auto tile_rows = [&](int t, long& row0, int& nvalid) {
+    if (t < np) {
+      row0 = static_cast<long>(t) * kKvTile;
+      nvalid = min(kKvTile, L - t * kKvTile);
+    } else {
+      row0 = L + static_cast<long>(t - np) * kKvTile;
+      nvalid = min(kKvTile, a.T - (t - np) * kKvTile);
+    }
+  };
+  uint4 kreg[CPT], vreg[CPT];
+  auto load_tile = [&](int t) {
+    long row0;
+    int nvalid;
+    tile_rows(t, row0, nvalid);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int q = tid + 256 * u;
+      const int r = q / CPR, c8 = q - r * CPR;
+      if (r < nvalid) {
+        const long off = (kvbase + row0 + r) * D + c8 * 8;
+        kreg[u] = *reinterpret_cast<const uint4*>(a.kc + off);
+        vreg[u] = *reinterpret_cast<const uint4*>(a.vc + off);
+      } else {
+        kreg[u] = make_uint4(0, 0, 0, 0);
+        vreg[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  int t = next_active(t_begin);
+  if (t < t_end) load_tile(t);
+  while (t < t_end) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int q = tid + 256 * u;
+      const int r = q / CPR, c8 = q - r * CPR;
+      *reinterpret_cast<uint4*>(Ks + r * KP + c8 * 8) = kreg[u];
+      *reinterpret_cast<uint4*>(Vs + r * KP + c8 * 8) = vreg[u];
+    }
+    __syncthreads();
+    const int tn = next_active(t + 1);
+    if (tn < t_end) load_tile(tn);
+
+    // ---- scores S^T = K Q^T for this tile ----
+    f32x4_t sacc[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) sacc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8_t kf = lds_read16(Ks + (cb * 16 + mm) * KP + kb * 32 + 8 * lg);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) sacc[mb][cb] = mfma16x16x32(kf, qf[mb][kb], sacc[mb][cb]);
+      }
+    }
+
+    // ---- mask, online softmax (log2 domain), P as the B operand of the second product ----
+    const bool is_tree = t >= np;
+    int nvalid;
+    long row0;
+    tile_rows(t, row0, nvalid);
+    uint32_t pb[2][2][4];   // [mb][ks][dword] packed bf16 pairs
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      uint64_t mw = 0;
+      if (is_tree && rvalid[mb]) mw = a.mask[static_cast<long>(node[mb]) * a.W + (t - np)];
+      float sv[4][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = cb * 16 + 4 * lg + j;
+          const bool vis = rvalid[mb] && c < nvalid && (!is_tree || ((mw >> c) & 1ull));
+          sv[cb][j] = vis ? sacc[mb][cb][j] * a.sl2 : -INFINITY;
+          mx = fmaxf(mx, sv[cb][j]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrow[mb], mx);
+      const float muse = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2f(mrow[mb] - muse);
+      mrow[mb] = mnew;
+      float ps = 0.f;
+      float pr[4][4];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = exp2f(sv[cb][j] - muse);
+          pr[cb][j] = bf16_to_f32(f32_to_bf16_rne(p));
+          ps += pr[cb][j];
+        }
+      lsum[mb] = lsum[mb] * alpha + ps;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) oacc[mb][db][j] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pb[mb][ks][0] = pack_bf16x2(pr[2 * ks][0], pr[2 * ks][1]);
+        pb[mb][ks][1] = pack_bf16x2(pr[2 * ks][2], pr[2 * ks][3]);
+        pb[mb][ks][2] = pack_bf16x2(pr[2 * ks + 1][0], pr[2 * ks + 1][1]);
+        pb[mb][ks][3] = pack_bf16x2(pr[2 * ks + 1][2], pr[2 * ks + 1][3]);
+      }
+    }
+
+    // ---- O^T += V^T P^T; contraction index 8*lg+e <-> tile column
+    //      ks*32 + (e < 4 ? 4*lg + e : 16 + 4*lg + e - 4), matching the score layout ----
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int crow = ks * 32 + 4 * lg + (mm >> 2);
+        const int dcol = db * 16 + 4 * (mm & 3);
+        const s16x4_t v0 = lds_read_tr(Vs + crow * KP + dcol);
+        const s16x4_t v1 = lds_read_tr(Vs + (crow + 16) * KP + dcol);
+        const uint4 av = make_uint4(
+            static_cast<uint16_t>(v0[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v0[1])) << 16),
+            static_cast<uint16_t>(v0[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(v0[3])) << 16),
+            static_cast<uint16_t>(v1[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v1[1])) << 16),
+            static_cast<uint16_t>(v1[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(v1[3])) << 16));
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const uint4 bv = make_uint4(pb[mb][ks][0], pb[mb][ks][1], pb[mb][ks][2], pb[mb][ks][3]);
+          oacc[mb][db] = mfma16x16x32(va, __builtin_bit_cast(bf16x8_t, bv), oacc[mb][db]);
+        }
+      }
+    }
+    t = tn;
+  }
+
+  // ---- finish: full row sums, then the output or this split's partial ----
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    float l = lsum[mb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int m = qt * kAttnRows + wave * 32 + mb * 16 + mm;
+    if (!rvalid[mb]) continue;
+    if (a.splits == 1) {
+      const float inv = 1.f / l;
+      const int hq = kvh * a.G + m % a.G;
+      uint16_t* orow = a.out + ((static_cast<long>(b) * a.Hq + hq) * a.T + node[mb]) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        uint2 w;
+        w.x = pack_bf16x2(oacc[mb][db][0] * inv, oacc[mb][db][1] * inv);
+        w.y = pack_bf16x2(oacc[mb][db][2] * inv, oacc[mb][db][3] * inv);
+        *reinterpret_cast<uint2*>(orow + db * 16 + 4 * lg) = w;
+      }
+    } else {
+      const long pr = ((static_cast<long>(split) * a.B + b) * a.Hkv + kvh) * a.Mpad + m;
+      float* op = a.o_part + pr * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<float4*>(op + db * 16 + 4 * lg) =
+            make_float4(oacc[mb][db][0], oacc[mb][db][1], oacc[mb][db][2], oacc[mb][db][3]);
+      if (lg == 0) a.ml_part[pr] = make_float2(mrow[mb], l);
+    }
+  }
+}
+
+// Merge of the K/V splits, in split order: one block of D threads per query row.
+template <typename OutT>
+__global__ void tree_attn_combine(const float* __restrict__ o_part, const float2* __restrict__ ml,
+                                  OutT* __restrict__ out, int B, int Hq, int Hkv, int T, int G,
+                                  int M, int Mpad, int splits, int D) {
+  const long rowid = blockIdx.x;   // over B * Hkv * M
+  const int m = static_cast<int>(rowid % M);
+  const long bk = rowid / M;       // b * Hkv + kvh
+  const int d = threadIdx.x;
+  float mx = -INFINITY;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, ml[(s * static_cast<long>(B) * Hkv + bk) * Mpad + m].x);
+  float l = 0.f, o = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const long pr = (s * static_cast<long>(B) * Hkv + bk) * Mpad + m;
+    const float2 v = ml[pr];
+    if (v.y == 0.f) continue;
+    const float f = exp2f(v.x - mx);
+    l += v.y * f;
+    o += o_part[pr * D + d] * f;
+  }
+  const int b = static_cast<int>(bk / Hkv), kvh = static_cast<int>(bk % Hkv);
+  const int node = m / G, hq = kvh * G + m % G;
+  const float r = o / l;
+  OutT* orow = out + ((static_cast<long>(b) * Hq + hq) * T + node) * D;
+  if constexpr (sizeof(OutT) == 2) orow[d] = f32_to_bf16_rne(r);
+  else orow[d] = r;
+}
+
+// fp32 path: one wave per (b, q head, node); lanes over the head dim, columns in order with an
+// online softmax.
+__global__ __launch_bounds__(64) void tree_attn_f32(const float* __restrict__ q,
+                                                    const float* __restrict__ kc,
+                                                    const float* __restrict__ vc,
+                                                    const int32_t* __restrict__ prefix_len,
+                                                    const uint64_t* __restrict__ mask, float* out,
+                                                    long lcap, int Hq, int Hkv, int T, int W,
+                                                    int D, float sl2, int Lmax) {
+  const long u = blockIdx.x;
+  const int i = static_cast<int>(u % T);
+  const int hq = static_cast<int>((u / T) % Hq);
+  const int b = static_cast<int>(u / (static_cast<long>(T) * Hq));
+  const int g = hq / (Hq / Hkv);
+  const int lane = threadIdx.x;
+  const int L = min(max(prefix_len[b], 0), Lmax);
+  const long base = (static_cast<long>(b) * Hkv + g) * lcap;
+  const float* qr = q + u * D;
+  float q0 = lane < D ? qr[lane] : 0.f, q1 = lane + 64 < D ? qr[lane + 64] : 0.f;
+  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (long j = 0; j < static_cast<long>(L) + T; ++j) {
+    if (j >= L) {
+      const int t = static_cast<int>(j - L);
+      if (!((mask[static_cast<long>(i) * W + t / 64] >> (t % 64)) & 1ull)) continue;
+    }
+    const float* kr = kc + (base + j) * D;
+    const float* vr = vc + (base + j) * D;
+    float s = (lane < D ? q0 * kr[lane] : 0.f) + (lane + 64 < D ? q1 * kr[lane + 64] : 0.f);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    s *= sl2;
+    const float mnew = fmaxf(m, s);
+    const float alpha = exp2f(m - mnew), p = exp2f(s - mnew);
+    l = l * alpha + p;
+    o0 = o0 * alpha + (lane < D ? p * vr[lane] : 0.f);
+    o1 = o1 * alpha + (lane + 64 < D ? p * vr[lane + 64] : 0.f);
+    m = mnew;
+  }
+  float* orow = out + u * D;
+  if (lane < D) orow[lane] = o0 / l;
+  if (lane + 64 < D) orow[lane + 64] = o1 / l;
+}
+
+AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_prefix_len) {
+  AttnPlan p{};
+  p.G = Hq / Hkv;
+  p.M = p.G * T;
+  p.qtiles = (p.M + kAttnRows - 1) / kAttnRows;
+  p.splits = 1;
+  if (dtype == 1) {
+    const long units = static_cast<long>(B) * Hkv * p.qtiles;
+    const int ntiles = (max_prefix_len + kKvTile - 1) / kKvTile + (T + kKvTile - 1) / kKvTile;
+    if (units < 256) {
+      long s = (384 + units - 1) / units;
+      s = s < ntiles / 2 ? s : ntiles / 2;
+      p.splits = s < 1 ? 1 : static_cast<int>(s);
+    }
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
+  const size_t rows = static_cast<size_t>(p.splits) * B * Hkv * p.qtiles * kAttnRows;
+  p.ws_o = take(p.splits > 1 ? rows * D * sizeof(float) : 0);
+  p.ws_ml = take(p.splits > 1 ? rows * sizeof(float2) : 0);
+  p.ws_cnt = 0;
+  p.total = off;
+  return p;
+}
+
+hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, int dtype,
+                                 const int32_t* prefix_len, int max_prefix_len, long lcap,
+                                 const uint64_t* mask, int B, int Hq, int Hkv, int T, int D,
+                                 float scale, void* out, char* ws, hipStream_t s) {
+  const AttnPlan P = attn_plan(dtype, B, Hq, Hkv, T, D, max_prefix_len);
+  const int W = (T + 63) / 64;
+  const float sl2 = scale * 1.4426950408889634f;
+  if (dtype == 0) {
+    tree_attn_f32<<<static_cast<unsigned>(static_cast<long>(B) * Hq * T), 64, 0, s>>>(
+        static_cast<const float*>(q), static_cast<const float*>(kc), static_cast<const float*>(vc),
+        prefix_len, mask, static_cast<float*>(out), lcap, Hq, Hkv, T, W, D, sl2, max_prefix_len);
+    return hipGetLastError();
+  }
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint16_t*>(kc);
+  a.vc = static_cast<const uint16_t*>(vc);
+  a.prefix_len = prefix_len;
+  a.mask = mask;
+  a.out = static_cast<uint16_t*>(out);
+  a.o_part = reinterpret_cast<float*>(ws + P.ws_o);
+  a.ml_part = reinterpret_cast<float2*>(ws + P.ws_ml);
+  a.lcap = lcap;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.T = T;
+  a.W = W;
+  a.G = P.G;
+  a.M = P.M;
+  a.Mpad = P.qtiles * kAttnRows;
+  a.qtiles = P.qtiles;
+  a.splits = P.splits;
+  a.nwork = B * Hkv * P.qtiles * P.splits;
+  a.sl2 = sl2;
+  a.Lmax = max_prefix_len;
+  const unsigned grid = static_cast<unsigned>(((a.nwork + 7) / 8) * 8);
+  if (D == 128) tree_attn_bf16<128><<<grid, 256, 0, s>>>(a);
+  else tree_attn_bf16<64><<<grid, 256, 0, s>>>(a);
+  if (P.splits > 1)
+    tree_attn_combine<uint16_t><<<static_cast<unsigned>(static_cast<long>(B) * Hkv * P.M), D, 0, s>>>(
+        a.o_part, a.ml_part, a.out, B, Hq, Hkv, T, P.G, P.M, a.Mpad, P.splits, D);
+  return hipGetLastError();
+}
+
+}  // namespace medusa

@@ -1,0 +1,378 @@
+// Typical acceptance over the verification logits, then the longest accepted prefix.
+//
+// Wiblog "Medusa multi-head speculative decoding", typical-acceptance section: a candidate is
+// accepted when its probability under the original model exceeds the minimum of a hard
+// threshold and an entropy-dependent one; the first token is taken greedily; temperature 0 is
+// greedy decoding.  Inference-flow section: walk from the root until the first rejection or a
+// leaf.  cnnetsun page: posterior_threshold (eps) and posterior_alpha (delta), returning
+// (best_candidate, accept_length).  Written out: p = softmax(l / T), H = -sum p ln p,
+// accept iff p(x) > min(eps, delta * exp(-H)).
+//
+// Only internal rows are read (a leaf's row judges no child).  One work-group per
+// (sequence, internal row, 2048-element chunk) computes in a single pass the chunk's max y,
+// S = sum 2^(y - max) and A = sum (y - max) 2^(y - max) with y = l * log2(e) / T, plus the
+// argmax; the last chunk of a row to finish merges the partials in chunk order, so
+// H = ln2 * (log2 S - A / S) and ln p(x) = ln2 * (y_x - max - log2 S), and decides the row's
+// children in the log domain; the last row of a sequence to finish scans the paths.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace medusa {
+
+constexpr int kAccThreads = 256;
+constexpr int kAccPerThread = 8;
+constexpr int kAccChunk = kAccThreads * kAccPerThread;  // 2048
+
+struct RowStat {   // partial softmax statistics of a set of elements (log2 units)
+  float m, S, A, pad;
+};
+
+__device__ __forceinline__ RowStat stat_merge(RowStat a, RowStat b) {
+  if (a.S == 0.f) return b;
+  if (b.S == 0.f) return a;
+  const float m = fmaxf(a.m, b.m);
+  const float fa = exp2f(a.m - m), fb = exp2f(b.m - m);
+  RowStat r;
+  r.m = m;
+  r.S = a.S * fa + b.S * fb;
+  r.A = (a.A + (a.m - m) * a.S) * fa + (b.A + (b.m - m) * b.S) * fb;
+  r.pad = 0.f;
+  return r;
+}
+
+__device__ __forceinline__ RowStat shfl_down_stat(RowStat s, int off) {
+  RowStat r;
+  r.m = __shfl_down(s.m, off);
+  r.S = __shfl_down(s.S, off);
+  r.A = __shfl_down(s.A, off);
+  r.pad = 0.f;
+  return r;
+}
+
+__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int off) {
+  uint32_t lo = __shfl_down(static_cast<uint32_t>(v), off);
+  uint32_t hi = __shfl_down(static_cast<uint32_t>(v >> 32), off);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Loads 8 logits starting at element idx0 of a row (fp32 out); invalid -> valid[e] = false.
+__device__ __forceinline__ void load8(const void* row, int dtype, long idx0, long V, float* x,
+                                      bool* valid) {
+  if (dtype == 1) {
+    const uint16_t* p = static_cast<const uint16_t*>(row);
+    if (idx0 + 8 <= V && (reinterpret_cast<uintptr_t>(p + idx0) & 15) == 0) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p + idx0);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))));
+        valid[e] = true;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        valid[e] = idx0 + e < V;
+        x[e] = valid[e] ? bf16_to_f32(p[idx0 + e]) : 0.f;
+      }
+    }
+  } else {
+    const float* p = static_cast<const float*>(row);
+    if (idx0 + 8 <= V && (reinterpret_cast<uintptr_t>(p + idx0) & 15) == 0) {
+      const float4 a = *reinterpret_cast<const float4*>(p + idx0);
+      const float4 b = *reinterpret_cast<const float4*>(p + idx0 + 4);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) valid[e] = true;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        valid[e] = idx0 + e < V;
+        x[e] = valid[e] ? p[idx0 + e] : 0.f;
+      }
+    }
+  }
+}
+
+struct AcceptArgs {
+  const void* logits;
+  int dtype, B, T;
+  long V;
+  const int32_t* tokens;
+  int n_int;
+  const int32_t* internal;
+  const int32_t* child_ptr;
+  const int32_t* child_idx;
+  const int32_t* paths;
+  const int32_t* path_len;
+  int n_paths, dmax;
+  int greedy;
+  float y_scale;      // log2(e) / temperature
+  float ln_eps, ln_delta;
+  int C;
+  RowStat* part_stat;     // [B][n_int][C]
+  uint64_t* part_arg;     // [B][n_int][C]
+  int32_t* dec;           // [B][T]
+  int32_t* rowarg;        // [B][T]
+  unsigned* cnt_row;      // [B][n_int]
+  unsigned* cnt_b;        // [B]
+  int32_t* last;          // [B]
+  int32_t* best;
+  int32_t* accept_len;
+};
+
+__global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
+  __shared__ RowStat s_stat[kAccThreads / 64];
+  __shared__ uint64_t s_arg[kAccThreads / 64];
+  __shared__ int s_last;
+  __shared__ RowStat s_row;
+  __shared__ uint64_t s_rowarg;
+  const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const int n = a.internal[r];
+  const int esz = a.dtype == 1 ? 2 : 4;
+  const char* row = static_cast<const char*>(a.logits) + (static_cast<long>(b) * a.T + n) * a.V * esz;
+  const long idx0 = static_cast<long>(c) * kAccChunk + static_cast<long>(threadIdx.x) * kAccPerThread;
+
+  float x[kAccPerThread];
+  bool valid[kAccPerThread];
+  load8(row, a.dtype, idx0, a.V, x, valid);
+
+  uint64_t arg = 0;
+#pragma unroll
+  for (int e = 0; e < kAccPerThread; ++e)
+    if (valid[e]) {
+      const uint64_t k = sel_key(x[e], static_cast<uint32_t>(idx0 + e));
+      arg = k > arg ? k : arg;
+    }
+  RowStat st{-INFINITY, 0.f, 0.f, 0.f};
+  if (!a.greedy) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kAccPerThread; ++e)
+      if (valid[e]) m = fmaxf(m, x[e] * a.y_scale);
+    if (m > -INFINITY) {
+      float S = 0.f, A = 0.f;
+#pragma unroll
+      for (int e = 0; e < kAccPerThread; ++e) {
+        if (!valid[e]) continue;
+        const float d = x[e] * a.y_scale - m;
+        const float p = exp2f(d);
+        if (p > 0.f) {
+          S += p;
+          A += d * p;
+        }
+      }
+      st = RowStat{m, S, A, 0.f};
+    }
+  }
+  // fixed-order reductions: within the wave toward lane 0, then across waves in wave order
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = shfl_down_u64(arg, off);
+    arg = o > arg ? o : arg;
+    if (!a.greedy) st = stat_merge(st, shfl_down_stat(st, off));
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_stat[w] = st;
+    s_arg[w] = arg;
+  }
+  __syncthreads();
+  const long pidx = (static_cast<long>(b) * a.n_int + r) * a.C + c;
+  if (threadIdx.x == 0) {
+    RowStat t = s_stat[0];
+    uint64_t g = s_arg[0];
+    for (int i = 1; i < kAccThreads / 64; ++i) {
+      t = stat_merge(t, s_stat[i]);
+      g = s_arg[i] > g ? s_arg[i] : g;
+    }
+    a.part_stat[pidx] = t;
+    a.part_arg[pidx] = g;
+    __threadfence();
+    s_last = atomicAdd(&a.cnt_row[static_cast<long>(b) * a.n_int + r], 1u) == static_cast<unsigned>(a.C - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- last chunk of this row: merge the partials in chunk order, decide the children ----
+  __threadfence();
+  if (threadIdx.x == 0) {
+    const long p0 = (static_cast<long>(b) * a.n_int + r) * a.C;
+    RowStat t = a.part_stat[p0];
+    uint64_t g = a.part_arg[p0];
+    for (int i = 1; i < a.C; ++i) {
+      t = stat_merge(t, a.part_stat[p0 + i]);
+      const uint64_t gi = a.part_arg[p0 + i];
+      g = gi > g ? gi : g;
+    }
+    s_row = t;
+    s_rowarg = g;
+    a.cnt_row[static_cast<long>(b) * a.n_int + r] = 0u;
+    a.rowarg[static_cast<long>(b) * a.T + n] = static_cast<int32_t>(sel_key_index(g));
+  }
+  __syncthreads();
+  const int c0 = a.child_ptr[n], c1 = a.child_ptr[n + 1];
+  for (int ci = c0 + threadIdx.x; ci < c1; ci += kAccThreads) {
+    const int child = a.child_idx[ci];
+    const int tok = a.tokens[static_cast<long>(b) * a.T + child];
+    int acc;
+    if (tok < 0 || tok >= a.V) {
+      acc = 0;                               // not a vocab id: never accepted, never read
+    } else if (a.greedy) {
+      acc = static_cast<uint32_t>(tok) == sel_key_index(s_rowarg);
+    } else {
+      const float l = a.dtype == 1 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[tok])
+                                   : reinterpret_cast<const float*>(row)[tok];
+      const float log2S = log2f(s_row.S);
+      const float ln2 = 0.69314718055994531f;
+      const float lnp = ln2 * (l * a.y_scale - s_row.m - log2S);
+      const float H = ln2 * (log2S - s_row.A / s_row.S);
+      const float lnthr = fminf(a.ln_eps, a.ln_delta - H);
+      acc = lnp > lnthr;
+    }
+    a.dec[static_cast<long>(b) * a.T + child] = acc;
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&a.cnt_b[b], 1u) == static_cast<unsigned>(a.n_int - 1);
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- last row of this sequence: longest accepted prefix over the paths ----
+  __threadfence();
+  __shared__ uint64_t scratch[kAccThreads / 64];
+  uint64_t bestk = 0;
+  for (int p = threadIdx.x; p < a.n_paths; p += kAccThreads) {
+    const int32_t* path = a.paths + static_cast<long>(p) * (a.dmax + 1);
+    const int len = a.path_len[p];
+    int k = 0;
+    while (k < len && a.dec[static_cast<long>(b) * a.T + path[k + 1]]) ++k;
+    const uint64_t key = (static_cast<uint64_t>(k) << 32) | (0xffffffffu - static_cast<uint32_t>(p));
+    bestk = key > bestk ? key : bestk;
+  }
+  bestk = block_max_u64<kAccThreads>(bestk, scratch);
+  if (threadIdx.x == 0) {
+    const int p = static_cast<int>(0xffffffffu - static_cast<uint32_t>(bestk & 0xffffffffu));
+    const int k = static_cast<int>(bestk >> 32);
+    a.best[b] = p;
+    a.accept_len[b] = k;
+    a.last[b] = a.paths[static_cast<long>(p) * (a.dmax + 1) + k];
+    a.cnt_b[b] = 0u;
+  }
+}
+
+// next_token[b] = argmax of the row of the last accepted node (lowest id on ties).  If that node
+// is internal its argmax is already known; otherwise the (leaf) row is read here.
+__global__ __launch_bounds__(kAccThreads) void accept_next_token(const void* logits, int dtype,
+                                                                 int T, long V, int C,
+                                                                 const int32_t* child_ptr,
+                                                                 const int32_t* last,
+                                                                 const int32_t* rowarg,
+                                                                 uint64_t* part, unsigned* cnt,
+                                                                 int32_t* next_token) {
+  __shared__ uint64_t scratch[kAccThreads / 64];
+  __shared__ int s_last;
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int n = last[b];
+  if (child_ptr[n + 1] > child_ptr[n]) {
+    if (c == 0 && threadIdx.x == 0) next_token[b] = rowarg[static_cast<long>(b) * T + n];
+    return;
+  }
+  const int esz = dtype == 1 ? 2 : 4;
+  const char* row = static_cast<const char*>(logits) + (static_cast<long>(b) * T + n) * V * esz;
+  const long idx0 = static_cast<long>(c) * kAccChunk + static_cast<long>(threadIdx.x) * kAccPerThread;
+  float x[kAccPerThread];
+  bool valid[kAccPerThread];
+  load8(row, dtype, idx0, V, x, valid);
+  uint64_t arg = 0;
+#pragma unroll
+  for (int e = 0; e < kAccPerThread; ++e)
+    if (valid[e]) {
+      const uint64_t k = sel_key(x[e], static_cast<uint32_t>(idx0 + e));
+      arg = k > arg ? k : arg;
+    }
+  arg = block_max_u64<kAccThreads>(arg, scratch);
+  if (threadIdx.x == 0) {
+    part[static_cast<long>(b) * C + c] = arg;
+    __threadfence();
+    s_last = atomicAdd(&cnt[b], 1u) == static_cast<unsigned>(C - 1);
+  }
+  __syncthreads();
+  if (!s_last || threadIdx.x != 0) return;
+  __threadfence();
+  uint64_t g = 0;
+  for (int i = 0; i < C; ++i) {
+    const uint64_t v = part[static_cast<long>(b) * C + i];
+    g = v > g ? v : g;
+  }
+  next_token[b] = static_cast<int32_t>(sel_key_index(g));
+  cnt[b] = 0u;
+}
+
+AcceptWs accept_ws_layout(int B, int T, long V, int n_internal) {
+  AcceptWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
+  const long C = (V + kAccChunk - 1) / kAccChunk;
+  w.chunks = static_cast<int>(C);
+  w.part = take((sizeof(RowStat) + sizeof(uint64_t)) * static_cast<size_t>(B) * n_internal * C);
+  w.dec = take(sizeof(int32_t) * static_cast<size_t>(B) * T * 2);   // decisions + row argmax
+  w.cnt_row = take(sizeof(unsigned) * static_cast<size_t>(B) * n_internal);
+  w.cnt_b = take(sizeof(unsigned) * B);
+  w.last = take(sizeof(int32_t) * B);
+  w.npart = take(sizeof(uint64_t) * static_cast<size_t>(B) * C);
+  w.cnt_nt = take(sizeof(unsigned) * B);
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, long V,
+                                 const int32_t* tokens, int n_internal, const int32_t* internal,
+                                 const int32_t* child_ptr, const int32_t* child_idx,
+                                 const int32_t* paths, const int32_t* path_len, int n_paths,
+                                 int dmax, float temperature, float eps, float delta,
+                                 int32_t* best, int32_t* accept_len, int32_t* next_token,
+                                 char* ws, hipStream_t s) {
+  const AcceptWs L = accept_ws_layout(B, T, V, n_internal);
+  const size_t nstat = static_cast<size_t>(B) * n_internal * L.chunks;
+  AcceptArgs a{};
+  a.logits = logits;
+  a.dtype = dtype;
+  a.B = B;
+  a.T = T;
+  a.V = V;
+  a.tokens = tokens;
+  a.n_int = n_internal;
+  a.internal = internal;
+  a.child_ptr = child_ptr;
+  a.child_idx = child_idx;
+  a.paths = paths;
+  a.path_len = path_len;
+  a.n_paths = n_paths;
+  a.dmax = dmax;
+  a.greedy = temperature == 0.f;
+  a.y_scale = a.greedy ? 0.f : static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
+  a.ln_eps = logf(eps);
+  a.ln_delta = logf(delta);
+  a.C = L.chunks;
+  a.part_stat = reinterpret_cast<RowStat*>(ws + L.part);
+  a.part_arg = reinterpret_cast<uint64_t*>(ws + L.part + sizeof(RowStat) * nstat);
+  a.dec = reinterpret_cast<int32_t*>(ws + L.dec);
+  a.rowarg = a.dec + static_cast<size_t>(B) * T;
+  a.cnt_row = reinterpret_cast<unsigned*>(ws + L.cnt_row);
+  a.cnt_b = reinterpret_cast<unsigned*>(ws + L.cnt_b);
+  a.last = reinterpret_cast<int32_t*>(ws + L.last);
+  a.best = best;
+  a.accept_len = accept_len;
+  accept_rows<<<dim3(L.chunks, n_internal, B), kAccThreads, 0, s>>>(a);
+  if (next_token)
+    accept_next_token<<<dim3(L.chunks, B), kAccThreads, 0, s>>>(
+        logits, dtype, T, V, L.chunks, child_ptr, a.last, a.rowarg,
+        reinterpret_cast<uint64_t*>(ws + L.npart), reinterpret_cast<unsigned*>(ws + L.cnt_nt),
+        next_token);
+  return hipGetLastError();
+}
+
+}  // namespace medusa

@@ -1,0 +1,56 @@
+"""One verification step on one stream: heads -> tree -> tree attention -> typical acceptance.
+
+Holds the device buffers and workspaces of a fixed shape so the timed loop allocates nothing.
+Inputs the step does not produce (the last hidden state, the tree tokens' Q/K/V inside the cache,
+the verification logits, the root tokens) are given by the caller.
+"""
+
+import torch
+
+from . import _lib
+
+
+class VerifyStep:
+    def __init__(self, *, B, hidden, vocab, K, topk, choices, Hq, Hkv, D, max_prefix_len,
+                 device="cuda"):
+        self.B, self.hidden, self.vocab, self.K, self.topk = B, hidden, vocab, K, topk
+        self.Hq, self.Hkv, self.D, self.max_prefix_len = Hq, Hkv, D, max_prefix_len
+        self.tree = _lib.Tree(choices, K, topk, device=device)
+        T = self.tree.T
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_ids = torch.zeros((B, K, topk), **i32)
+        self.topk_logits = torch.zeros((B, K, topk), dtype=torch.float32, device=device)
+        self.logits = torch.zeros((B, K, vocab), dtype=torch.float32, device=device)
+        self.tokens = torch.zeros((B, T), **i32)
+        self.position_ids = torch.zeros((B, T), **i32)
+        self.best = torch.zeros(B, **i32)
+        self.accept_length = torch.zeros(B, **i32)
+        self.next_token = torch.zeros(B, **i32)
+        self.ws_heads = _lib.workspace(_lib.medusa_heads_workspace(B, hidden, vocab, K, topk), device)
+        self.ws_attn = _lib.workspace(_lib.tree_attention_workspace(B, Hq, Hkv, T, D, max_prefix_len), device)
+        self.ws_acc = _lib.workspace(
+            _lib.typical_accept_workspace(B, T, vocab, self.tree.dims["n_internal"]), device)
+
+    def heads(self, h, w1, b1, w2, stream=None):
+        _lib.medusa_heads(h, w1, b1, w2, self.topk, self.topk_ids, self.ws_heads, logits=self.logits,
+                          topk_logits=self.topk_logits, stream=stream)
+
+    def build(self, root_tokens, prefix_len, stream=None):
+        _lib.build_tree(self.tree, self.topk_ids, root_tokens, prefix_len, self.tokens,
+                        self.position_ids, stream=stream)
+
+    def attention(self, q, k_cache, v_cache, prefix_len, out, stream=None):
+        _lib.tree_attention(q, k_cache, v_cache, prefix_len, self.max_prefix_len, self.tree.mask,
+                            out, self.ws_attn, stream=stream)
+
+    def accept(self, verif_logits, temperature, eps=0.09, delta=0.3, next_token=True, stream=None):
+        _lib.typical_accept(verif_logits, self.tokens, self.tree, temperature, eps, delta, self.best,
+                            self.accept_length, self.ws_acc,
+                            next_token=self.next_token if next_token else None, stream=stream)
+
+    def run(self, *, h, w1, b1, w2, root_tokens, prefix_len, q, k_cache, v_cache, attn_out,
+            verif_logits, temperature, eps=0.09, delta=0.3, stream=None):
+        self.heads(h, w1, b1, w2, stream)
+        self.build(root_tokens, prefix_len, stream)
+        self.attention(q, k_cache, v_cache, prefix_len, attn_out, stream)
+        self.accept(verif_logits, temperature, eps, delta, stream=stream)

@@ -53,6 +53,20 @@ def row_threshold(z_row, eps, delta):
     return p, H, thr
 
 
+def scan_paths(static, accepted_b):
+    """Longest run of accepted nodes below the root along each root-to-leaf path.  Returns
+    (best path = lowest index among the longest, its accept length, last accepted node)."""
+    paths, path_len = static["paths"], static["path_len"]
+    lens = []
+    for p, row in enumerate(paths):
+        n = 0
+        while n < path_len[p] and accepted_b[row[n + 1]]:
+            n += 1
+        lens.append(n)
+    best = int(np.argmax(lens))             # first (lowest) index among the maxima
+    return best, lens[best], paths[best][lens[best]]
+
+
 def typical_accept(logits, dtype, tokens, static, temperature, eps=0.09, delta=0.3):
     """logits [B,T,V] (stored dtype), tokens [B][T].  Returns a dict with best_candidate,
     accept_length, next_token (all [B]) plus per-child diagnostics:
@@ -86,16 +100,7 @@ def typical_accept(logits, dtype, tokens, static, temperature, eps=0.09, delta=0
     alen = np.zeros(B, np.int32)
     nxt = np.zeros(B, np.int32)
     for b in range(B):
-        lens = []
-        for p, row in enumerate(paths):
-            n = 0
-            while n < path_len[p] and accepted[b, row[n + 1]]:
-                n += 1
-            lens.append(n)
-        best[b] = int(np.argmax(lens))      # first (lowest) index among the maxima
-        alen[b] = lens[best[b]]
-        last = paths[best[b]][alen[b]]
-        row = _row_f64(logits, dtype, b, last)
-        nxt[b] = _argmax_lowest(row)
+        best[b], alen[b], last = scan_paths(static, accepted[b])
+        nxt[b] = _argmax_lowest(_row_f64(logits, dtype, b, last))
     return dict(best_candidate=best, accept_length=alen, next_token=nxt, accepted=accepted,
                 margin=margin, argmax=argmax, entropy=H_all, threshold=thr_all)

@@ -1,28 +1,36 @@
-"""Seeded generators.  Every draw comes from numpy's PCG64, one stream per tensor group.
+"""Seeded generators.  Every draw comes from numpy's PCG64 in independent 2**22-element blocks.
 
-Recipe (stated once here and in the design notes):
-  * stream = Generator(PCG64(SeedSequence([seed, stream_id]))).
-  * Normals are drawn in fp64 in chunks of 2**24 elements, scaled, cast to fp32, then rounded
-    to bf16 with round-to-nearest-even when the workload is bf16.  bf16 tensors are held as
-    uint16 bit patterns.
-  * stream 0: h [B,Hd] ~ N(0,1)
-  * stream 1: for each head k in order: W1[k] [Hd,Hd], b1[k] [Hd], W2[k] [V,Hd], all ~ N(0, w_std^2)
-  * stream 2: prefix K then prefix V, each [B,Hkv,L_b,D] ~ N(0,1) (per sequence b in order)
-  * stream 3: tree Q [B,Hq,T,D], tree K, tree V [B,Hkv,T,D] ~ N(0,1)
+Recipe:
+  * A tensor is filled block by block (2**22 elements, row-major order).  Block i of tensor t of
+    stream s draws float32 standard normals from Generator(PCG64(SeedSequence([seed, s, t, i]))),
+    so blocks can be drawn in parallel threads and any block can be regenerated alone.
+  * Normals are scaled by their std in fp32, then rounded to bf16 with round-to-nearest-even when
+    the workload is bf16.  bf16 tensors are held as uint16 bit patterns.
+  * stream 0: h [B,Hd] ~ N(0,1)                                       (tensor 0)
+  * stream 1: head k: W1[k] [Hd,Hd] (tensor 3k), b1[k] [Hd] (3k+1), W2[k] [V,Hd] (3k+2),
+              all ~ N(0, w_std^2)
+  * stream 2: K cache (tensor 0), V cache (tensor 1) [B,Hkv,Lcap,D] ~ N(0,1); rows [0, L_b) are
+              the prefix, rows past L_b+T are filler that a correct kernel never reads
+  * stream 3: tree Q [B,Hq,T,D] (tensor 0), tree K (1), tree V (2) [B,Hkv,T,D] ~ N(0,1); tree
+              K/V are written over cache rows [L_b, L_b+T)
   * stream 4: root tokens [B], uniform integers in [0,V)
-  * stream 5: verification logits [B,T,V] ~ N(0, logit_std^2)
+  * stream 5: verification logits [B,T,V] ~ N(0, logit_std^2)        (tensor 0)
   * stream 6: one uniform per (b, non-root node) in node order; the node's own token gets
-    +boost in the row of its parent when the draw is below boost_p.
-  * stream 7: cache rows beyond L_b+T (never read by a correct kernel) ~ N(0,1)
+              +boost in its parent's row when the draw is below boost_p.
 """
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-CHUNK = 1 << 24
+BLOCK = 1 << 22
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
-def rng_for(seed, stream):
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(stream)])))
+def rng_for(seed, stream, tensor=0, block=0):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+        [int(seed), int(stream), int(tensor), int(block)])))
 
 
 def f32_to_bf16_bits(a):
@@ -37,40 +45,45 @@ def bf16_bits_to_f32(b):
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _normals_into(rng, out_flat, std, dtype):
-    """Fill out_flat (float32 or uint16 view) with N(0, std^2) draws, chunk by chunk."""
-    n = out_flat.size
-    for s in range(0, n, CHUNK):
-        m = min(CHUNK, n - s)
-        x = (rng.standard_normal(m) * std).astype(np.float32)
-        if dtype == "bf16":
-            out_flat[s:s + m] = f32_to_bf16_bits(x)
-        else:
-            out_flat[s:s + m] = x
+def _fill_block(out_flat, seed, stream, tensor, i, std, dtype):
+    s = i * BLOCK
+    m = min(BLOCK, out_flat.size - s)
+    x = rng_for(seed, stream, tensor, i).standard_normal(m, dtype=np.float32)
+    x *= np.float32(std)
+    out_flat[s:s + m] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def fill_normals(out, seed, stream, tensor, std, dtype):
+    flat = out.reshape(-1)
+    nb = (flat.size + BLOCK - 1) // BLOCK
+    if nb <= 1:
+        for i in range(nb):
+            _fill_block(flat, seed, stream, tensor, i, std, dtype)
+    else:
+        with ThreadPoolExecutor(min(_THREADS, nb)) as ex:
+            list(ex.map(lambda i: _fill_block(flat, seed, stream, tensor, i, std, dtype), range(nb)))
+    return out
 
 
 def _empty(shape, dtype):
     return np.empty(shape, dtype=np.float32 if dtype == "f32" else np.uint16)
 
 
-def normals(rng, shape, std, dtype):
-    a = _empty(shape, dtype)
-    _normals_into(rng, a.reshape(-1), std, dtype)
-    return a
+def normals(shape, seed, stream, tensor, std, dtype):
+    return fill_normals(_empty(shape, dtype), seed, stream, tensor, std, dtype)
 
 
 def gen_head_inputs(cfg, seed=None):
     """h [B,Hd]; W1 [K,Hd,Hd] ([out,in]); b1 [K,Hd]; W2 [K,V,Hd] ([out,in])."""
     seed = cfg.seed if seed is None else seed
-    h = normals(rng_for(seed, 0), (cfg.B, cfg.Hd), 1.0, cfg.dtype)
-    r1 = rng_for(seed, 1)
+    h = normals((cfg.B, cfg.Hd), seed, 0, 0, 1.0, cfg.dtype)
     w1 = _empty((cfg.K, cfg.Hd, cfg.Hd), cfg.dtype)
     b1 = _empty((cfg.K, cfg.Hd), cfg.dtype)
     w2 = _empty((cfg.K, cfg.V, cfg.Hd), cfg.dtype)
     for k in range(cfg.K):
-        _normals_into(r1, w1[k].reshape(-1), cfg.w_std, cfg.dtype)
-        _normals_into(r1, b1[k].reshape(-1), cfg.w_std, cfg.dtype)
-        _normals_into(r1, w2[k].reshape(-1), cfg.w_std, cfg.dtype)
+        fill_normals(w1[k], seed, 1, 3 * k, cfg.w_std, cfg.dtype)
+        fill_normals(b1[k], seed, 1, 3 * k + 1, cfg.w_std, cfg.dtype)
+        fill_normals(w2[k], seed, 1, 3 * k + 2, cfg.w_std, cfg.dtype)
     return dict(h=h, w1=w1, b1=b1, w2=w2)
 
 
@@ -89,26 +102,14 @@ def gen_attention_inputs(cfg, T, seed=None, prefix_lens=None, lcap=None):
     need = int(pl.max()) + T
     lcap = need if lcap is None else int(lcap)
     assert lcap >= need
-    kc = _empty((B, Hkv, lcap, D), cfg.dtype)
-    vc = _empty((B, Hkv, lcap, D), cfg.dtype)
-    r2 = rng_for(seed, 2)
-    for cache in (kc, vc):
-        for b in range(B):
-            for g in range(Hkv):
-                _normals_into(r2, cache[b, g, :pl[b]].reshape(-1), 1.0, cfg.dtype)
-    r3 = rng_for(seed, 3)
-    q = normals(r3, (B, Hq, T, D), 1.0, cfg.dtype)
-    kt = normals(r3, (B, Hkv, T, D), 1.0, cfg.dtype)
-    vt = normals(r3, (B, Hkv, T, D), 1.0, cfg.dtype)
-    r7 = rng_for(seed, 7)
+    kc = normals((B, Hkv, lcap, D), seed, 2, 0, 1.0, cfg.dtype)
+    vc = normals((B, Hkv, lcap, D), seed, 2, 1, 1.0, cfg.dtype)
+    q = normals((B, Hq, T, D), seed, 3, 0, 1.0, cfg.dtype)
+    kt = normals((B, Hkv, T, D), seed, 3, 1, 1.0, cfg.dtype)
+    vt = normals((B, Hkv, T, D), seed, 3, 2, 1.0, cfg.dtype)
     for b in range(B):
         kc[b, :, pl[b]:pl[b] + T] = kt[b]
         vc[b, :, pl[b]:pl[b] + T] = vt[b]
-        rest = lcap - (pl[b] + T)
-        if rest > 0:
-            for cache in (kc, vc):
-                for g in range(Hkv):
-                    _normals_into(r7, cache[b, g, pl[b] + T:].reshape(-1), 1.0, cfg.dtype)
     return dict(q=q, k_cache=kc, v_cache=vc, prefix_len=pl, lcap=lcap)
 
 
@@ -123,8 +124,7 @@ def gen_verif_logits(cfg, parent, tokens, seed=None):
     tokens = np.asarray(tokens)
     B, V = cfg.B, cfg.V
     T = parent.shape[0]
-    x = np.empty((B, T, V), np.float32)
-    _normals_into(rng_for(seed, 5), x.reshape(-1), cfg.logit_std, "f32")
+    x = normals((B, T, V), seed, 5, 0, cfg.logit_std, "f32")
     u = rng_for(seed, 6).random((B, T - 1))
     for b in range(B):
         for c in range(1, T):

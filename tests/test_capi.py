@@ -1,0 +1,119 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/medusa.h declares, and
+its host-only paths (sizes, tree dims, argument validation) behave as documented.  No compute
+call is made here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    import medusa_head_speculative_amd as m
+    so = os.path.join(os.path.dirname(m.__file__), "libmedusa_hip.so")
+    if not os.path.exists(so):
+        from medusa_head_speculative_amd import build
+        build.build()
+    m.load()
+    return m
+
+
+def _header_functions():
+    txt = open(os.path.join(ROOT, "include", "medusa.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", txt, flags=re.M)) -
+                  {"defined"})
+
+
+def test_exports_every_declared_function(m):
+    names = _header_functions()
+    assert set(names) == set(m.EXPORTS), names
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(m.__file__), "libmedusa_hip.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _choices(ch):
+    md = max(len(c) for c in ch)
+    a = np.full((len(ch), md), -1, np.int32)
+    for i, c in enumerate(ch):
+        a[i, :len(c)] = c
+    return a, md
+
+
+def _dims(m, ch, K, topk):
+    L = m.load()
+    a, md = _choices(ch)
+    t = m._lib.medusa_tree()
+    rc = L.medusa_tree_dims(ctypes.c_void_p(a.ctypes.data), len(ch), md, K, topk, ctypes.byref(t))
+    return rc, t
+
+
+def test_tree_dims_match_the_oracle(m):
+    import oracle
+    from synth import load_tree_choices
+    for name, K in [("c0", 2), ("c1", 4), ("c2", 5), ("c3", 3), ("c4", 3)]:
+        ch = load_tree_choices(name)
+        rc, t = _dims(m, ch, K, 10)
+        st = oracle.build_static(ch, 10, K)
+        assert rc == 0
+        assert (t.T, t.W, t.n_paths, t.dmax) == (st["T"], st["W"], len(st["paths"]), st["dmax"])
+        assert t.n_internal == sum(1 for c in st["children"] if c)
+
+
+@pytest.mark.parametrize("ch,K,topk", [
+    ([[0, 0]], 3, 3),              # not prefix-closed
+    ([[0], [3]], 3, 3),            # rank >= topk
+    ([[0], [0, 0], [0, 0, 0]], 2, 3),   # depth > K
+    ([[0], [0]], 3, 3),            # duplicate
+])
+def test_tree_dims_rejects_malformed_lists(m, ch, K, topk):
+    rc, _ = _dims(m, ch, K, topk)
+    assert rc == -4
+    assert m.load().medusa_last_error().decode()
+
+
+def test_workspace_queries(m):
+    assert m.medusa_heads_workspace(1, 4096, 32000, 4, 10) > 4 * 32000 * 4
+    assert m.medusa_heads_workspace(9, 4096, 32000, 4, 10) == 0      # B > 8
+    assert m.medusa_heads_workspace(1, 4016, 32000, 4, 10) == 0      # hidden % 32
+    assert m.medusa_heads_workspace(1, 4096, 32000, 4, 65) == 0      # topk > 64
+    assert m.tree_attention_workspace(1, 32, 32, 65, 128, 1024) > 0
+    assert m.tree_attention_workspace(1, 32, 5, 65, 128, 1024) == 0  # Hq % Hkv
+    assert m.tree_attention_workspace(1, 32, 32, 65, 96, 1024) == 0  # D
+    assert m.typical_accept_workspace(1, 65, 32000, 32) > 0
+    assert m.typical_accept_workspace(1, 65, 32000, 65) == 0
+
+
+def test_invalid_arguments_fail_before_any_launch(m):
+    L = m.load()
+    p = ctypes.c_void_p(16)          # never dereferenced: validation fails first
+    assert L.medusa_heads(p, p, p, p, 7, 1, 64, 100, 1, 1, None, p, None, p, 1 << 20, None) == -3
+    assert L.medusa_heads(None, p, p, p, 1, 1, 64, 100, 1, 1, None, p, None, p, 1 << 20, None) == -1
+    assert L.medusa_heads(p, p, p, p, 1, 1, 64, 100, 9, 1, None, p, None, p, 1 << 20, None) == -2
+    assert L.medusa_heads(p, p, p, p, 1, 1, 64, 100, 1, 1, None, p, None, p, 16, None) == -5
+    assert "workspace" in L.medusa_last_error().decode()
+    assert L.tree_attention(p, p, p, 1, p, 10, 5, p, 1, 4, 4, 9, 64, 0.0, p, p, 1 << 20, None) == -2
+    assert L.tree_attention(p, p, p, 1, p, 10, 100, p, 1, 4, 3, 9, 64, 0.0, p, p, 1 << 20, None) == -2
+    t = m._lib.medusa_tree(T=9, W=1, n_paths=6, dmax=2, n_internal=3, mask=16, parent=16, depth=16,
+                           rank=16, paths=16, path_len=16, child_ptr=16, child_idx=16, internal=16)
+    args = [p, 1, 1, 9, 100, p, ctypes.byref(t)]
+    outs = [p, p, p, p, 1 << 20, None]
+    assert L.typical_accept(*args, -1.0, 0.09, 0.3, *outs) == -1
+    assert L.typical_accept(*args, 0.7, 1.5, 0.3, *outs) == -1
+    assert L.typical_accept(*args, 0.7, 0.09, 0.0, *outs) == -1
+    assert L.typical_accept(p, 1, 1, 8, 100, p, ctypes.byref(t), 0.7, 0.09, 0.3, *outs) == -2
+    assert L.typical_accept(*args, 0.7, 0.09, 0.3, p, p, p, p, 8, None) == -5
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    import medusa_head_speculative_amd._lib as lib
+    monkeypatch.setattr(lib, "_lib", None)
+    monkeypatch.setattr(lib, "LIBPATH", str(tmp_path / "nope.so"))
+    with pytest.raises(ImportError):
+        lib.load()

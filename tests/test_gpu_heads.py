@@ -1,0 +1,118 @@
+"""GPU parity of medusa_heads (heads + top-k) against the fp64 oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import check_topk, dev, host, lib, say, tol
+from synth import gen_head_inputs, get_config
+from synth.configs import custom
+from synth.gen import normals
+
+pytestmark = pytest.mark.gpu
+
+
+def run_heads(m, inp, K, V, topk):
+    import torch
+    h = dev(inp["h"])
+    B, hd = inp["h"].shape
+    ws = m.workspace(m.medusa_heads_workspace(B, hd, V, K, topk))
+    logits = torch.full((B, K, V), float("nan"), dtype=torch.float32, device="cuda")
+    ids = torch.full((B, K, topk), -1, dtype=torch.int32, device="cuda")
+    tl = torch.zeros((B, K, topk), dtype=torch.float32, device="cuda")
+    m.medusa_heads(h, dev(inp["w1"]), dev(inp["b1"]), dev(inp["w2"]), topk, ids, ws, logits=logits,
+                   topk_logits=tl)
+    torch.cuda.synchronize()
+    return host(logits), host(ids), host(tl)
+
+
+@pytest.mark.parametrize("ci", [0, 1, 2, 3, 4])
+def test_heads_full_size(ci):
+    cfg = get_config(ci)
+    m = lib()
+    inp = gen_head_inputs(cfg)
+    _, l64 = oracle.heads(inp["h"], inp["w1"], inp["b1"], inp["w2"], cfg.dtype)
+    say("heads full size", cfg.name, dict(B=cfg.B, Hd=cfg.Hd, V=cfg.V, K=cfg.K, k=cfg.topk))
+    lg, ids, tl = run_heads(m, inp, cfg.K, cfg.V, cfg.topk)
+    err = float(np.abs(lg - l64).max())
+    print(f"{cfg.name}: max |logit - oracle| = {err:.3e}")
+    assert err <= tol(cfg.dtype)
+    rows, ties = check_topk(ids, l64, cfg.topk)
+    print(f"{cfg.name}: top-k rows {rows}, tie rows {ties}")
+    assert ties < rows
+    np.testing.assert_array_equal(tl, np.take_along_axis(lg, ids, axis=-1))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_init_heads_reproduce_lm_head(dtype):
+    # Ultralytics "Medusa Heads": zero W1/b1 and W2 = LM head -> each head equals lm_head(h)
+    hd, V, K, topk = 256, 1000, 3, 8
+    m = lib()
+    lm = normals((V, hd), 77, 1, 2, 0.02, dtype)
+    h = normals((1, hd), 77, 0, 0, 1.0, dtype)
+    zeros = np.zeros((K, hd, hd), lm.dtype)
+    inp = dict(h=h, w1=zeros, b1=np.zeros((K, hd), lm.dtype),
+               w2=np.ascontiguousarray(np.broadcast_to(lm, (K, V, hd))))
+    say("zero-init heads", dtype)
+    lg, ids, _ = run_heads(m, inp, K, V, topk)
+    base = oracle.project(lm, dtype, (h.astype(np.float64) if dtype == "f32" else
+                                      (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)))
+    printed = [bool(np.array_equal(lg[:, k], lg[:, 0])) for k in range(K)]
+    assert printed == [True, True, True]
+    assert float(np.abs(lg[:, 0] - base).max()) <= tol(dtype)
+    check_topk(ids, np.broadcast_to(base[:, None, :], (1, K, V)).copy(), topk)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,hd,V,K,topk", [
+    (1, 32, 1, 1, 1), (3, 64, 63, 2, 5), (8, 96, 65, 3, 64), (2, 128, 257, 8, 10),
+    (5, 4096, 4097, 2, 10), (7, 160, 16384 + 5, 1, 33),
+])
+def test_heads_ragged_shapes(dtype, B, hd, V, K, topk):
+    m = lib()
+    cfg = custom(dtype=dtype, B=B, Hd=hd, V=V, K=K, topk=topk, w_std=1.0 / np.sqrt(hd), seed=B * 7 + K)
+    inp = gen_head_inputs(cfg)
+    _, l64 = oracle.heads(inp["h"], inp["w1"], inp["b1"], inp["w2"], dtype)
+    say("heads ragged", dtype, B, hd, V, K, topk)
+    lg, ids, _ = run_heads(m, inp, K, V, topk)
+    assert float(np.abs(lg - l64).max()) <= tol(dtype)
+    check_topk(ids, l64, topk)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_heads_equal_logits_resolve_to_lower_id(dtype):
+    from synth.gen import bf16_bits_to_f32, f32_to_bf16_bits
+    m = lib()
+    hd, V, K, topk = 64, 300, 2, 12
+    cfg = custom(dtype=dtype, B=2, Hd=hd, V=V, K=K, topk=topk, w_std=0.1, seed=5)
+    inp = gen_head_inputs(cfg)
+    w2 = inp["w2"]
+    tied = (10, 150, 200, 299)
+    for k in range(K):                      # four identical rows, scaled x4 so they rank high
+        row = w2[k, 10].copy()
+        if dtype == "f32":
+            big = row * np.float32(4)
+        else:
+            big = f32_to_bf16_bits(bf16_bits_to_f32(row) * np.float32(4))
+        for v in tied:
+            w2[k, v] = big
+    say("heads exact ties", dtype)
+    lg, ids, _ = run_heads(m, inp, K, V, topk)
+    for b in range(2):
+        for k in range(K):
+            row = lg[b, k]
+            assert len({float(row[v]) for v in tied}) == 1
+            order = sorted(range(V), key=lambda v: (-row[v], v))[:topk]
+            assert ids[b, k].tolist() == order
+
+
+def test_heads_deterministic():
+    m = lib()
+    cfg = custom(dtype="bf16", B=4, Hd=1024, V=5000, K=3, topk=10, w_std=1 / 32, seed=9)
+    inp = gen_head_inputs(cfg)
+    say("heads determinism")
+    a = run_heads(m, inp, 3, 5000, 10)
+    b = run_heads(m, inp, 3, 5000, 10)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                              y.view(np.uint32) if y.dtype == np.float32 else y)
