@@ -103,6 +103,31 @@ int medusa_heads(const void* h, const void* w1, const void* b1, const void* w2, 
                  int hidden, long vocab, int K, int topk, float* logits, int32_t* topk_ids,
                  float* topk_logits, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The same heads with bf16 weights pre-packed once by medusa_pack_weights (a device-side
+ * reordering of the [out, in] matrices into the matrix-core operand order, so every weight is
+ * read as part of one contiguous stream).  Semantics, arguments and limits are those of
+ * medusa_heads with dtype = MEDUSA_BF16; only w1_packed / w2_packed differ:
+ *   w1_packed  medusa_packed_weight_bytes(K, hidden, hidden) bytes from w1
+ *   w2_packed  medusa_packed_weight_bytes(K, vocab, hidden) bytes from w2
+ */
+int medusa_heads_packed(const void* h, const void* w1_packed, const void* b1,
+                        const void* w2_packed, int B, int hidden, long vocab, int K, int topk,
+                        float* logits, int32_t* topk_ids, float* topk_logits, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Bytes of the packed form of K bf16 matrices of [rows, hidden] (0 on invalid sizes). */
+size_t medusa_packed_weight_bytes(int K, long rows, int hidden);
+
+/*
+ * Packs w (device, [K, rows, hidden] bf16, [out, in]) into `packed` (device,
+ * medusa_packed_weight_bytes(K, rows, hidden) bytes): per head, per 16-row tile, per 32-column
+ * block, the 64 lanes' 16-byte operands back to back, rows past `rows` zero-filled:
+ *   packed[k][tile][kb][lane][e] = w[k][16 tile + lane % 16][32 kb + 8 (lane / 16) + e].
+ * Done once per model, outside the decode loop.  Limits as medusa_heads.
+ */
+int medusa_pack_weights(const void* w, int K, long rows, int hidden, void* packed, void* stream);
+
 /* ---------------------------------------------------------------------------------------- *
  * 2. The candidate tree
  * ---------------------------------------------------------------------------------------- */
@@ -218,6 +243,32 @@ int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
                    float posterior_threshold, float posterior_alpha, int32_t* best_candidate,
                    int32_t* accept_length, int32_t* next_token, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------- *
+ * Measurement hook (not part of the method)
+ * ---------------------------------------------------------------------------------------- */
+
+/* The kernels the four entry points launch, for per-kernel timing. */
+typedef enum {
+  MEDUSA_KERNEL_HEADS_W1 = 0,      /* medusa_heads: first layer, r = h + SiLU(W1 h + b1)   */
+  MEDUSA_KERNEL_HEADS_W2 = 1,      /* medusa_heads: vocab projection, logits = W2 r        */
+  MEDUSA_KERNEL_TOPK = 2,          /* medusa_heads: per-head top-k                         */
+  MEDUSA_KERNEL_TREE_GATHER = 3,   /* build_tree: tokens and position ids                  */
+  MEDUSA_KERNEL_ATTENTION = 4,     /* tree_attention: main kernel                          */
+  MEDUSA_KERNEL_ATTN_COMBINE = 5,  /* tree_attention: merge of K/V splits (when split)     */
+  MEDUSA_KERNEL_ACCEPT = 6,        /* typical_accept: row statistics, decisions, path scan */
+  MEDUSA_KERNEL_NEXT_TOKEN = 7,    /* unused: next_token is found inside the accept kernel */
+  MEDUSA_KERNEL_COUNT = 8
+} medusa_kernel;
+
+/*
+ * While set, every launch of kernel `which` made by the calling thread records the HIP event
+ * `before` (a hipEvent_t) on the call's stream just before the launch and `after` just after
+ * it, so hipEventElapsedTime(before, after) is that launch's duration.  NULL for both clears
+ * the hook.  The events are owned by the caller and must outlive their use.
+ * Returns MEDUSA_ERR_ARG for an unknown kernel id or a single NULL event.
+ */
+int medusa_set_kernel_events(int which, void* before, void* after);
 
 #ifdef __cplusplus
 }

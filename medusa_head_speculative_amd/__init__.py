@@ -9,12 +9,16 @@ from ._lib import (  # noqa: F401
     BF16,
     EXPORTS,
     F32,
+    KERNELS,
     MedusaError,
     Tree,
     build_tree,
     load,
     medusa_heads,
+    medusa_heads_packed,
+    pack_weights,
     medusa_heads_workspace,
+    set_kernel_events,
     tree_attention,
     tree_attention_workspace,
     typical_accept,

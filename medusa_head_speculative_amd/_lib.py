@@ -36,7 +36,11 @@ class medusa_tree(ctypes.Structure):
 
 EXPORTS = ["medusa_last_error", "medusa_heads_workspace", "medusa_heads", "medusa_tree_dims",
            "build_tree", "tree_attention_workspace", "tree_attention",
-           "typical_accept_workspace", "typical_accept"]
+           "typical_accept_workspace", "typical_accept", "medusa_set_kernel_events",
+           "medusa_heads_packed", "medusa_packed_weight_bytes", "medusa_pack_weights"]
+
+KERNELS = ["heads_w1", "heads_w2", "topk", "tree_gather", "attention", "attn_combine", "accept",
+           "next_token"]
 
 _lib = None
 
@@ -70,6 +74,14 @@ def load():
     L.typical_accept_workspace.argtypes = [i, i, l, i]
     L.typical_accept.restype = i
     L.typical_accept.argtypes = [vp, i, i, i, l, vp, tp, f, f, f, vp, vp, vp, vp, sz, vp]
+    L.medusa_set_kernel_events.restype = i
+    L.medusa_heads_packed.restype = i
+    L.medusa_heads_packed.argtypes = [vp, vp, vp, vp, i, i, l, i, i, vp, vp, vp, vp, sz, vp]
+    L.medusa_packed_weight_bytes.restype = sz
+    L.medusa_packed_weight_bytes.argtypes = [i, l, i]
+    L.medusa_pack_weights.restype = i
+    L.medusa_pack_weights.argtypes = [vp, i, l, i, vp, vp]
+    L.medusa_set_kernel_events.argtypes = [i, vp, vp]
     _lib = L
     return L
 
@@ -119,6 +131,26 @@ def medusa_heads(h, w1, b1, w2, topk, topk_ids, ws, logits=None, topk_logits=Non
     _check(load().medusa_heads(_ptr(h), _ptr(w1), _ptr(b1), _ptr(w2), dtype_code(h), B, hd, V, K,
                                topk, _ptr(logits), _ptr(topk_ids), _ptr(topk_logits), _ptr(ws),
                                ws.numel(), _stream(stream)))
+
+
+def pack_weights(w, stream=None):
+    """w [K, rows, hidden] bf16 -> packed bf16 tensor (flat) for medusa_heads_packed."""
+    K, rows, hd = w.shape
+    n = load().medusa_packed_weight_bytes(K, rows, hd)
+    if n == 0:
+        raise MedusaError(-2, f"cannot pack a [{K}, {rows}, {hd}] weight")
+    out = torch.empty(n // 2, dtype=torch.bfloat16, device=w.device)
+    _check(load().medusa_pack_weights(_ptr(w), K, rows, hd, _ptr(out), _stream(stream)))
+    return out
+
+
+def medusa_heads_packed(h, w1_packed, b1, w2_packed, vocab, K, topk, topk_ids, ws, logits=None,
+                        topk_logits=None, stream=None):
+    """As medusa_heads with weights from pack_weights (bf16)."""
+    B, hd = h.shape
+    _check(load().medusa_heads_packed(_ptr(h), _ptr(w1_packed), _ptr(b1), _ptr(w2_packed), B, hd,
+                                      vocab, K, topk, _ptr(logits), _ptr(topk_ids),
+                                      _ptr(topk_logits), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------------------------
@@ -205,3 +237,14 @@ def typical_accept(logits, tokens, tree, temperature, posterior_threshold, poste
                                  ctypes.byref(tree.c), temperature, posterior_threshold,
                                  posterior_alpha, _ptr(best_candidate), _ptr(accept_length),
                                  _ptr(next_token), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------------------------
+def set_kernel_events(kernel, before=None, after=None):
+    """Measurement hook: record torch.cuda.Events around every launch of `kernel` (a name from
+    KERNELS) on this thread; None clears it.  The events must have been recorded once (so that
+    torch has created them)."""
+    which = KERNELS.index(kernel)
+    b = ctypes.c_void_p(before.cuda_event) if before is not None else None
+    a = ctypes.c_void_p(after.cuda_event) if after is not None else None
+    _check(load().medusa_set_kernel_events(which, b, a))

@@ -135,6 +135,13 @@ int upload(T* dst, const std::vector<T>& src, const char* name) {
 
 }  // namespace
 
+namespace medusa {
+EventHook* event_hooks() {
+  static thread_local EventHook hooks[kKernelCount];
+  return hooks;
+}
+}  // namespace medusa
+
 extern "C" {
 
 const char* medusa_last_error(void) { return g_err; }
@@ -166,10 +173,43 @@ int medusa_heads(const void* h, const void* w1, const void* b1, const void* w2, 
   if (!workspace || workspace_bytes < need)
     return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   if ((rc = check_pending())) return rc;
-  return launched(medusa::launch_heads(h, w1, b1, w2, dtype, B, hidden, vocab, K, topk, logits,
+  return launched(medusa::launch_heads(h, w1, b1, w2, dtype, 0, B, hidden, vocab, K, topk, logits,
                                        topk_ids, topk_logits, static_cast<char*>(workspace),
                                        static_cast<hipStream_t>(stream)),
                   "medusa_heads");
+}
+
+size_t medusa_packed_weight_bytes(int K, long rows, int hidden) {
+  if (K < 1 || K > 8 || rows < 1 || rows >= (1l << 31) || hidden < 32 || hidden > 16384 || hidden % 32)
+    return 0;
+  return medusa::packed_weight_bytes(K, rows, hidden);
+}
+
+int medusa_pack_weights(const void* w, int K, long rows, int hidden, void* packed, void* stream) {
+  if (!w || !packed) return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
+  if (medusa_packed_weight_bytes(K, rows, hidden) == 0)
+    return fail(MEDUSA_ERR_SHAPE, "K = %d, rows = %ld, hidden = %d", K, rows, hidden);
+  int rc;
+  if ((rc = check_pending())) return rc;
+  return launched(medusa::launch_pack_weights(w, K, rows, hidden, packed, static_cast<hipStream_t>(stream)),
+                  "medusa_pack_weights");
+}
+
+int medusa_heads_packed(const void* h, const void* w1_packed, const void* b1,
+                        const void* w2_packed, int B, int hidden, long vocab, int K, int topk,
+                        float* logits, int32_t* topk_ids, float* topk_logits, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!h || !w1_packed || !b1 || !w2_packed || !topk_ids) return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
+  int rc = heads_shape(B, hidden, vocab, K, topk);
+  if (rc) return rc;
+  const size_t need = medusa::heads_ws_layout(B, hidden, vocab, K, topk).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if ((rc = check_pending())) return rc;
+  return launched(medusa::launch_heads(h, w1_packed, b1, w2_packed, MEDUSA_BF16, 1, B, hidden, vocab,
+                                       K, topk, logits, topk_ids, topk_logits,
+                                       static_cast<char*>(workspace), static_cast<hipStream_t>(stream)),
+                  "medusa_heads_packed");
 }
 
 // ---- tree -----------------------------------------------------------------------------------
@@ -304,6 +344,16 @@ int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
                                                 static_cast<char*>(workspace),
                                                 static_cast<hipStream_t>(stream)),
                   "typical_accept");
+}
+
+// ---- measurement hook ------------------------------------------------------------------------
+int medusa_set_kernel_events(int which, void* before, void* after) {
+  if (which < 0 || which >= medusa::kKernelCount) return fail(MEDUSA_ERR_ARG, "kernel id %d", which);
+  if ((before == nullptr) != (after == nullptr)) return fail(MEDUSA_ERR_ARG, "give both events or neither");
+  medusa::event_hooks()[which].before = static_cast<hipEvent_t>(before);
+  medusa::event_hooks()[which].after = static_cast<hipEvent_t>(after);
+  g_err[0] = '\0';
+  return MEDUSA_OK;
 }
 
 }  // extern "C"

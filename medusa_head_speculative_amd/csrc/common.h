@@ -59,6 +59,29 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Wave-wide max of 64-bit keys with DPP row steps (xor 1, xor 2, rotate 4, rotate 8 inside each
+// 16-lane row) and a 4-way scalar combine of the rows; every lane gets the result.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, 0xF, 0xF, false));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+  v = umax64(v, dpp_u64<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = umax64(v, dpp_u64<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = umax64(v, dpp_u64<0x124>(v));   // row_ror:4
+  v = umax64(v, dpp_u64<0x128>(v));   // row_ror:8
+  return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
 // Max over a block of NT threads (NT a multiple of 64, <= 1024); every thread gets the result.
 // `scratch` holds NT/64 entries.  Contains __syncthreads().
 template <int NT>

@@ -11,13 +11,15 @@
 // 16 columns, hi and lo bf16 halves of the fp32 vector side by side, so r keeps ~17 bits of
 // mantissa and each weight is loaded once with 16-byte loads.  The fp32 path (small models)
 // uses plain FMAs.
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace medusa {
 
 // ------------------------------------------------------------------------------------------
-// Epilogue shared by the two projections
+// Epilogue shared by the projections
 // ------------------------------------------------------------------------------------------
 struct HeadsEpi {
   int mode;               // 0: first layer (u -> r), 1: vocab projection (-> logits)
@@ -29,7 +31,7 @@ struct HeadsEpi {
   const void* h;          // [B][hd] dtype            (mode 0)
   int dtype;
   float* r_out;           // [B][K][hd] fp32          (mode 0)
-  uint16_t* xfrag;        // [K][hd/32][64][8] bf16   (mode 0, bf16 path only)
+  uint16_t* xs;           // [K][2B][hd] bf16         (mode 0, bf16 path): hi(r) rows, then lo(r)
   float* logits;          // [B][K][rows] fp32        (mode 1)
 };
 
@@ -44,38 +46,44 @@ __device__ __forceinline__ void heads_epilogue(const HeadsEpi& ep, int k, long r
     const float u = y + load_elem(ep.b1, ep.dtype, static_cast<long>(k) * ep.hd + i);
     const float r = load_elem(ep.h, ep.dtype, static_cast<long>(b) * ep.hd + i) + u / (1.0f + expf(-u));
     ep.r_out[(static_cast<long>(b) * ep.K + k) * ep.hd + i] = r;
-    if (ep.xfrag) {
-      // B-operand fragment of the vocab projection: kblock i/32, lane group (i%32)/8, element i%8;
-      // column b carries hi(r), column B+b carries lo(r) = r - hi(r); columns >= 2B are zero.
+    if (ep.xs) {
+      // the vocab projection's vector operand: hi(r) and lo(r) = r - hi(r) as bf16 rows
       const uint16_t hi = f32_to_bf16_rne(r);
       const uint16_t lo = f32_to_bf16_rne(r - bf16_to_f32(hi));
-      const long kb = i >> 5;
-      const int g = (i >> 3) & 3, e = i & 7;
-      uint16_t* base = ep.xfrag + ((static_cast<long>(k) * (ep.hd >> 5) + kb) * 64) * 8;
-      base[(g * 16 + b) * 8 + e] = hi;
-      base[(g * 16 + ep.B + b) * 8 + e] = lo;
-      if (b == 0)
-        for (int n = 2 * ep.B; n < 16; ++n) base[(g * 16 + n) * 8 + e] = 0;
+      uint16_t* base = ep.xs + static_cast<long>(k) * 2 * ep.B * ep.hd + i;
+      base[static_cast<long>(b) * ep.hd] = hi;
+      base[static_cast<long>(ep.B + b) * ep.hd] = lo;
     }
   } else {
     ep.logits[(static_cast<long>(b) * ep.K + k) * ep.rows + row] = y;
   }
 }
 
+// B operand of v_mfma_f32_16x16x32_bf16 for contraction block kb: lane l holds column n = l%16,
+// contraction indices 8*(l/16)..+7.  Columns n < ncols are rows of xs ([ncols][hd] bf16: the B
+// vectors for the first layer, or hi then lo halves of r for the vocab projection); the others
+// are zero.
+__device__ __forceinline__ bf16x8_t x_operand(const uint16_t* xp, int kb) {
+  return xp ? load_bf16x8(xp + kb * 32) : zero_bf16x8();
+}
+
+__device__ __forceinline__ bf16x8_t load_bf16x8_nt(const uint16_t* p) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // ------------------------------------------------------------------------------------------
-// bf16 weights on the matrix cores
+// bf16 weights in the [out, in] layout, on the matrix cores
 // ------------------------------------------------------------------------------------------
 // Work-group: 4 waves, 16*TPW consecutive rows of one head; wave w takes the w-th quarter of the
 // hidden dim for all of them, so the 4 partial tiles are summed in LDS in a fixed order.
-// MFMA v_mfma_f32_16x16x32_bf16, A = 16 weight rows x 32 columns (lane l: row l%16, columns
-// 8*(l/16)..+7: one 16-byte load), B = 32 columns x 16 vectors, D lane l: rows 4*(l/16)+j of
-// vector column l%16.
-// XFROM_H: the B operand is built from h itself (bf16, so lo = 0); otherwise it is read from the
-// fragment buffer written by the first layer's epilogue.
-template <int TPW, bool XFROM_H>
+// A = 16 weight rows x 32 columns (lane l: row l%16, columns 8*(l/16)..+7: one 16-byte
+// nontemporal load, the weights are read once), D lane l: rows 4*(l/16)+j of column l%16.
+template <int TPW>
 __global__ __launch_bounds__(256) void heads_gemv_bf16(const uint16_t* __restrict__ W,
                                                         const uint16_t* __restrict__ xsrc,
-                                                        HeadsEpi ep) {
+                                                        int ncols, HeadsEpi ep) {
   __shared__ float red[4][TPW][64][4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -93,8 +101,8 @@ __global__ __launch_bounds__(256) void heads_gemv_bf16(const uint16_t* __restric
     if (r > ep.rows - 1) r = ep.rows - 1;          // ragged tail: valid address, result dropped
     wrow[t] = W + (static_cast<long>(k) * ep.rows + r) * hd + g * 8;
   }
-  const uint16_t* xf = XFROM_H ? (n < ep.B ? xsrc + static_cast<long>(n) * hd + g * 8 : nullptr)
-                               : xsrc + (static_cast<long>(k) * nkb * 64 + lane) * 8;
+  const uint16_t* xp = n < ncols ? xsrc + (static_cast<long>(k) * ncols * ep.mode + n) * hd + g * 8
+                                 : nullptr;
 
   f32x4_t acc[TPW];
 #pragma unroll
@@ -106,9 +114,8 @@ __global__ __launch_bounds__(256) void heads_gemv_bf16(const uint16_t* __restric
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) a[u][t] = load_bf16x8(wrow[t] + (kb + u) * 32);
-      if (XFROM_H) x[u] = xf ? load_bf16x8(xf + (kb + u) * 32) : zero_bf16x8();
-      else x[u] = load_bf16x8(xf + static_cast<long>(kb + u) * 512);
+      for (int t = 0; t < TPW; ++t) a[u][t] = load_bf16x8_nt(wrow[t] + (kb + u) * 32);
+      x[u] = x_operand(xp, kb + u);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -116,11 +123,10 @@ __global__ __launch_bounds__(256) void heads_gemv_bf16(const uint16_t* __restric
       for (int t = 0; t < TPW; ++t) acc[t] = mfma16x16x32(a[u][t], x[u], acc[t]);
   }
   for (; kb < kb1; ++kb) {
-    bf16x8_t a[TPW], x;
+    bf16x8_t a[TPW];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) a[t] = load_bf16x8(wrow[t] + kb * 32);
-    if (XFROM_H) x = xf ? load_bf16x8(xf + kb * 32) : zero_bf16x8();
-    else x = load_bf16x8(xf + static_cast<long>(kb) * 512);
+    for (int t = 0; t < TPW; ++t) a[t] = load_bf16x8_nt(wrow[t] + kb * 32);
+    const bf16x8_t x = x_operand(xp, kb);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) acc[t] = mfma16x16x32(a[t], x, acc[t]);
   }
@@ -133,16 +139,133 @@ __global__ __launch_bounds__(256) void heads_gemv_bf16(const uint16_t* __restric
 
   // outputs of this work-group: 16*TPW rows x B vectors; y = sum over waves of (hi + lo) columns
   const int B = ep.B;
+  const int lo_off = ncols > B ? B : 0;             // the first layer's vector has no lo part
   for (int o = threadIdx.x; o < 16 * TPW * B; o += 256) {
     const int rr = o / B, b = o - rr * B;
     const int t = rr >> 4, m = rr & 15;
     const int lh = (m >> 2) * 16 + b, j = m & 3;
     float y = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) y += red[w][t][lh][j] + red[w][t][lh + B][j];
+    for (int w = 0; w < 4; ++w) y += lo_off ? red[w][t][lh][j] + red[w][t][lh + lo_off][j] : red[w][t][lh][j];
     const long row = row0 + rr;
     if (row < ep.rows) heads_epilogue(ep, k, row, b, y);
   }
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16 weights pre-packed in MFMA fragment order
+// ------------------------------------------------------------------------------------------
+// Packed layout (medusa_pack_weights): per head, per 16-row tile, per 32-column block, the 64
+// lanes' 16-byte A fragments back to back:
+//   P[k][tile][kb][lane][e] = W[k][16*tile + lane%16][32*kb + 8*(lane/16) + e]  (0 past the rows)
+// so one wave-wide 16-byte load reads 1 KB of contiguous memory and the weights of a tile are one
+// contiguous stream: the pattern the HBM streams fastest.
+// KSPLIT = 4: the 4 waves of a work-group split the contraction for the same TPW tiles (for short
+// matrices, to keep enough bytes in flight) and meet in LDS; KSPLIT = 1: every wave owns TPW
+// tiles and the whole contraction.
+template <int TPW, int U, int KSPLIT>
+__global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restrict__ Wp,
+                                                          const uint16_t* __restrict__ xsrc,
+                                                          int ncols, HeadsEpi ep) {
+  __shared__ float red[KSPLIT == 4 ? 4 : 1][TPW][64][4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int k = blockIdx.y;
+  const long ntiles = (ep.rows + 15) >> 4;
+  const long t0 = (KSPLIT == 4 ? static_cast<long>(blockIdx.x) : static_cast<long>(blockIdx.x) * 4 + wave) * TPW;
+  if (KSPLIT == 1 && t0 >= ntiles) return;
+  const int hd = ep.hd;
+  const int nkb = hd >> 5;
+  const int kb0 = KSPLIT == 4 ? (wave * nkb) >> 2 : 0;
+  const int kb1 = KSPLIT == 4 ? ((wave + 1) * nkb) >> 2 : nkb;
+  const int g = lane >> 4, n = lane & 15;
+
+  const uint16_t* ap[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    long tt = t0 + t;
+    if (tt > ntiles - 1) tt = ntiles - 1;             // ragged: valid address, result dropped
+    ap[t] = Wp + (static_cast<long>(k) * ntiles + tt) * nkb * 512 + lane * 8;
+  }
+  const uint16_t* xp = n < ncols ? xsrc + (static_cast<long>(k) * ncols * ep.mode + n) * hd + g * 8
+                                 : nullptr;
+
+  f32x4_t acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  int kb = kb0;
+  for (; kb + U <= kb1; kb += U) {
+    bf16x8_t a[U][TPW], x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) a[u][t] = load_bf16x8_nt(ap[t] + static_cast<long>(kb + u) * 512);
+      x[u] = x_operand(xp, kb + u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) acc[t] = mfma16x16x32(a[u][t], x[u], acc[t]);
+  }
+  for (; kb < kb1; ++kb) {
+    bf16x8_t a[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) a[t] = load_bf16x8_nt(ap[t] + static_cast<long>(kb) * 512);
+    const bf16x8_t x = x_operand(xp, kb);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) acc[t] = mfma16x16x32(a[t], x, acc[t]);
+  }
+
+  const int B = ep.B;
+  const int lo_off = ncols > B ? B : 0;
+  if (KSPLIT == 4) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[wave][t][lane][j] = acc[t][j];
+    __syncthreads();
+    for (int o = threadIdx.x; o < 16 * TPW * B; o += 256) {
+      const int rr = o / B, b = o - rr * B;
+      const int t = rr >> 4, m = rr & 15;
+      const int lh = (m >> 2) * 16 + b, j = m & 3;
+      float y = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) y += lo_off ? red[w][t][lh][j] + red[w][t][lh + lo_off][j] : red[w][t][lh][j];
+      const long row = t0 * 16 + rr;
+      if (row < ep.rows) heads_epilogue(ep, k, row, b, y);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float y = acc[t][j];
+        const float ylo = __shfl_down(y, lo_off > 0 ? lo_off : 1);
+        if (lo_off) y += ylo;
+        const long row = (t0 + t) * 16 + 4 * g + j;
+        if (n < B && row < ep.rows) heads_epilogue(ep, k, row, n, y);
+      }
+    }
+  }
+}
+
+// Repack [K][rows][hd] bf16 weights into the fragment order above; one thread per 16 bytes.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ W, long rows,
+                                                           int hd, long total16,
+                                                           uint16_t* __restrict__ P) {
+  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= total16) return;
+  const int nkb = hd >> 5;
+  const long ntiles = (rows + 15) >> 4;
+  const int lane = static_cast<int>(i & 63);
+  const long kb = (i >> 6) % nkb;
+  const long tile_all = (i >> 6) / nkb;              // k * ntiles + tile
+  const long k = tile_all / ntiles, tile = tile_all - k * ntiles;
+  const long row = tile * 16 + (lane & 15);
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (row < rows) v = *reinterpret_cast<const uint4*>(W + (k * rows + row) * hd + kb * 32 + 8 * (lane >> 4));
+  *reinterpret_cast<uint4*>(P + i * 8) = v;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -188,61 +311,85 @@ __global__ __launch_bounds__(256) void heads_gemv_f32(const float* __restrict__ 
 // ------------------------------------------------------------------------------------------
 // top-k over each row of the fp32 logits [R][V]
 // ------------------------------------------------------------------------------------------
-// Grid (C chunks, R rows).  Each work-group selects its chunk's k best keys by k rounds of a
-// block-wide max (a round takes the best key below the previous winner; keys are unique), then
-// the last work-group of the row to finish merges the C*k candidates the same way.
+// Selection keys are unique (value, then lower id), so "the k best" is a well defined set and
+// the rounds below need no tie handling.  One round picks the best key below the previous
+// winner with a wave-wide max (DPP, no LDS).
+//
+// Grid (C chunks of 4096, R rows).  Phase 1: each wave keeps the k best of its 1024 elements;
+// wave 0 merges the 4 waves' lists into the chunk's k best.  Phase 2: the last work-group of the
+// row to finish (atomic counter) merges the C*k chunk candidates, 1024 at a time, each batch
+// together with the running best list.
 constexpr int kTopkThreads = 256;
 constexpr int kTopkPerThread = 16;
 constexpr int kTopkChunk = kTopkThreads * kTopkPerThread;
+
+// k rounds over NK keys per lane plus an optional running list (lane t < k holds entry t).
+// Returns the new list in lanes 0..k-1 (lane t: t-th best); other lanes get 0.
+template <int NK>
+__device__ __forceinline__ uint64_t wave_select(const uint64_t (&keys)[NK], uint64_t running, int k) {
+  const int lane = threadIdx.x & 63;
+  uint64_t prev = ~0ull, mine = 0;
+  for (int t = 0; t < k; ++t) {
+    uint64_t best = running < prev ? running : 0ull;
+#pragma unroll
+    for (int e = 0; e < NK; ++e)
+      if (keys[e] < prev && keys[e] > best) best = keys[e];
+    best = wave_max_u64_dpp(best);
+    if (lane == t) mine = best;
+    prev = best;
+  }
+  return mine;
+}
 
 __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restrict__ logits, long V,
                                                           int k, int C, uint64_t* __restrict__ part,
                                                           unsigned* __restrict__ counters,
                                                           int32_t* __restrict__ ids,
                                                           float* __restrict__ vals) {
-  __shared__ uint64_t scratch[kTopkThreads / 64];
+  __shared__ uint64_t s_cand[4][64];
   __shared__ int s_last;
   const int row = blockIdx.y, c = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* x = logits + static_cast<long>(row) * V;
   uint64_t keys[kTopkPerThread];
+  const long base = static_cast<long>(c) * kTopkChunk + wave * 1024;
 #pragma unroll
   for (int e = 0; e < kTopkPerThread; ++e) {
-    const long idx = static_cast<long>(c) * kTopkChunk + e * kTopkThreads + threadIdx.x;
+    const long idx = base + e * 64 + lane;
     keys[e] = idx < V ? sel_key(x[idx], static_cast<uint32_t>(idx)) : 0ull;
   }
-  uint64_t prev = ~0ull;
-  for (int t = 0; t < k; ++t) {
-    uint64_t best = 0;
+  s_cand[wave][lane] = wave_select(keys, 0ull, k);
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t k4[4];
 #pragma unroll
-    for (int e = 0; e < kTopkPerThread; ++e)
-      if (keys[e] < prev && keys[e] > best) best = keys[e];
-    best = block_max_u64<kTopkThreads>(best, scratch);
-    if (threadIdx.x == 0) part[(static_cast<long>(row) * C + c) * k + t] = best;
-    prev = best;
+    for (int w = 0; w < 4; ++w) k4[w] = lane < k ? s_cand[w][lane] : 0ull;
+    const uint64_t mine = wave_select(k4, 0ull, k);
+    if (lane < k) part[(static_cast<long>(row) * C + c) * k + lane] = mine;
+    __threadfence();
+    if (lane == 0) s_last = atomicAdd(&counters[row], 1u) == static_cast<unsigned>(C - 1);
   }
-  __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&counters[row], 1u) == static_cast<unsigned>(C - 1));
-  __syncthreads();
-  if (!s_last) return;
+  if (!s_last || wave != 0) return;
+
+  // ---- phase 2 (one wave): the C*k chunk candidates, 1024 per batch ----
   __threadfence();
   const uint64_t* pr = part + static_cast<long>(row) * C * k;
   const long n = static_cast<long>(C) * k;
-  prev = ~0ull;
-  for (int t = 0; t < k; ++t) {
-    uint64_t best = 0;
-    for (long i = threadIdx.x; i < n; i += kTopkThreads) {
-      const uint64_t v = __builtin_nontemporal_load(pr + i);
-      if (v < prev && v > best) best = v;
+  uint64_t running = 0;
+  for (long b0 = 0; b0 < n; b0 += 1024) {
+#pragma unroll
+    for (int e = 0; e < kTopkPerThread; ++e) {
+      const long i = b0 + e * 64 + lane;
+      keys[e] = i < n ? pr[i] : 0ull;
     }
-    best = block_max_u64<kTopkThreads>(best, scratch);
-    if (threadIdx.x == 0) {
-      ids[static_cast<long>(row) * k + t] = static_cast<int32_t>(sel_key_index(best));
-      if (vals) vals[static_cast<long>(row) * k + t] = sel_key_value(best);
-    }
-    prev = best;
+    running = wave_select(keys, running, k);
   }
-  if (threadIdx.x == 0) counters[row] = 0u;
+  if (lane < k) {
+    ids[static_cast<long>(row) * k + lane] = static_cast<int32_t>(sel_key_index(running));
+    if (vals) vals[static_cast<long>(row) * k + lane] = sel_key_value(running);
+  }
+  if (lane == 0) counters[row] = 0u;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -253,7 +400,7 @@ HeadsWs heads_ws_layout(int B, int hd, long V, int K, int topk) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
   w.r = take(sizeof(float) * B * K * hd);
-  w.xfrag = take(sizeof(uint16_t) * static_cast<size_t>(K) * hd * 32);
+  w.xs = take(sizeof(uint16_t) * static_cast<size_t>(K) * 2 * B * hd);
   w.logits = take(sizeof(float) * static_cast<size_t>(B) * K * V);
   const long C = (V + kTopkChunk - 1) / kTopkChunk;
   w.part = take(sizeof(uint64_t) * static_cast<size_t>(B) * K * C * topk);
@@ -263,32 +410,103 @@ HeadsWs heads_ws_layout(int B, int hd, long V, int K, int topk) {
   return w;
 }
 
+size_t packed_weight_bytes(int K, long rows, int hd) {
+  return static_cast<size_t>(K) * ((rows + 15) / 16) * 16 * hd * sizeof(uint16_t);
+}
+
+hipError_t launch_pack_weights(const void* w, int K, long rows, int hd, void* packed, hipStream_t s) {
+  const long total16 = static_cast<long>(packed_weight_bytes(K, rows, hd) / 16);
+  pack_weights_kernel<<<static_cast<unsigned>((total16 + 255) / 256), 256, 0, s>>>(
+      static_cast<const uint16_t*>(w), rows, hd, total16, static_cast<uint16_t*>(packed));
+  return hipGetLastError();
+}
+
+// Packed-layout kernel variants (tiles per wave, unroll, contraction split); selectable for
+// tuning through MEDUSA_W1_VARIANT / MEDUSA_W2_VARIANT.
+struct PackedVariant {
+  int tpw, u, ksplit;
+};
+static const PackedVariant kPackedVariants[] = {
+    {1, 8, 4}, {2, 8, 4}, {1, 8, 1}, {2, 4, 1}, {2, 8, 1}, {4, 4, 1}, {4, 8, 1}, {1, 16, 1}};
+constexpr int kDefaultW1Variant = 0;
+constexpr int kDefaultW2VariantSmallB = 2;   // B <= 2: one tile per wave, 8 blocks in flight
+constexpr int kDefaultW2Variant = 4;         // B > 2: two tiles per wave share the x operand
+
+static int variant_from_env(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v) return dflt;
+  const int i = atoi(v);
+  return (i >= 0 && i < static_cast<int>(sizeof(kPackedVariants) / sizeof(kPackedVariants[0]))) ? i : dflt;
+}
+
+static void launch_packed(int variant, const uint16_t* Wp, const uint16_t* x, int ncols,
+                          const HeadsEpi& ep, hipStream_t s) {
+  const PackedVariant v = kPackedVariants[variant];
+  const long ntiles = (ep.rows + 15) / 16;
+  const long per_block = v.ksplit == 4 ? v.tpw : 4L * v.tpw;
+  const dim3 grid(static_cast<unsigned>((ntiles + per_block - 1) / per_block), ep.K);
+#define MEDUSA_PACKED_CASE(I, T, U_, S_) \
+  case I: heads_gemv_packed<T, U_, S_><<<grid, 256, 0, s>>>(Wp, x, ncols, ep); break;
+  switch (variant) {
+    MEDUSA_PACKED_CASE(0, 1, 8, 4)
+    MEDUSA_PACKED_CASE(1, 2, 8, 4)
+    MEDUSA_PACKED_CASE(2, 1, 8, 1)
+    MEDUSA_PACKED_CASE(3, 2, 4, 1)
+    MEDUSA_PACKED_CASE(4, 2, 8, 1)
+    MEDUSA_PACKED_CASE(5, 4, 4, 1)
+    MEDUSA_PACKED_CASE(6, 4, 8, 1)
+    default: MEDUSA_PACKED_CASE(7, 1, 16, 1)
+  }
+#undef MEDUSA_PACKED_CASE
+}
+
 hipError_t launch_heads(const void* h, const void* w1, const void* b1, const void* w2, int dtype,
-                        int B, int hd, long V, int K, int topk, float* logits, int32_t* topk_ids,
-                        float* topk_logits, char* ws, hipStream_t s) {
+                        int packed, int B, int hd, long V, int K, int topk, float* logits,
+                        int32_t* topk_ids, float* topk_logits, char* ws, hipStream_t s) {
   const HeadsWs L = heads_ws_layout(B, hd, V, K, topk);
   float* r = reinterpret_cast<float*>(ws + L.r);
-  uint16_t* xfrag = reinterpret_cast<uint16_t*>(ws + L.xfrag);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xs);
   float* lg = logits ? logits : reinterpret_cast<float*>(ws + L.logits);
   uint64_t* part = reinterpret_cast<uint64_t*>(ws + L.part);
   unsigned* counters = reinterpret_cast<unsigned*>(ws + L.counters);
 
-  HeadsEpi e1{0, K, hd, hd, B, b1, h, dtype, r, dtype == 1 ? xfrag : nullptr, nullptr};
+  HeadsEpi e1{0, K, hd, hd, B, b1, h, dtype, r, dtype == 1 ? xs : nullptr, nullptr};
   HeadsEpi e2{1, K, V, hd, B, nullptr, nullptr, dtype, nullptr, nullptr, lg};
-  if (dtype == 1) {
+  const uint16_t* hb = static_cast<const uint16_t*>(h);
+  if (dtype == 1 && packed) {
+    static const int v1 = variant_from_env("MEDUSA_W1_VARIANT", kDefaultW1Variant);
+    static const int v2_env = variant_from_env("MEDUSA_W2_VARIANT", -1);
+    const int v2 = v2_env >= 0 ? v2_env : (B <= 2 ? kDefaultW2VariantSmallB : kDefaultW2Variant);
+    hook_before(K_HEADS_W1, s);
+    launch_packed(v1, static_cast<const uint16_t*>(w1), hb, B, e1, s);
+    hook_after(K_HEADS_W1, s);
+    hook_before(K_HEADS_W2, s);
+    launch_packed(v2, static_cast<const uint16_t*>(w2), xs, 2 * B, e2, s);
+    hook_after(K_HEADS_W2, s);
+  } else if (dtype == 1) {
     constexpr int TPW1 = 2, TPW2 = 2;
-    heads_gemv_bf16<TPW1, true><<<dim3((hd + 16 * TPW1 - 1) / (16 * TPW1), K), 256, 0, s>>>(
-        static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(h), e1);
-    heads_gemv_bf16<TPW2, false><<<dim3((V + 16 * TPW2 - 1) / (16 * TPW2), K), 256, 0, s>>>(
-        static_cast<const uint16_t*>(w2), xfrag, e2);
+    hook_before(K_HEADS_W1, s);
+    heads_gemv_bf16<TPW1><<<dim3((hd + 16 * TPW1 - 1) / (16 * TPW1), K), 256, 0, s>>>(
+        static_cast<const uint16_t*>(w1), hb, B, e1);
+    hook_after(K_HEADS_W1, s);
+    hook_before(K_HEADS_W2, s);
+    heads_gemv_bf16<TPW2><<<dim3((V + 16 * TPW2 - 1) / (16 * TPW2), K), 256, 0, s>>>(
+        static_cast<const uint16_t*>(w2), xs, 2 * B, e2);
+    hook_after(K_HEADS_W2, s);
   } else {
+    hook_before(K_HEADS_W1, s);
     heads_gemv_f32<<<dim3((hd + 3) / 4, K), 256, 0, s>>>(static_cast<const float*>(w1),
                                                          static_cast<const float*>(h), hd, 0, e1);
+    hook_after(K_HEADS_W1, s);
+    hook_before(K_HEADS_W2, s);
     heads_gemv_f32<<<dim3((V + 3) / 4, K), 256, 0, s>>>(static_cast<const float*>(w2), r,
                                                         static_cast<long>(K) * hd, hd, e2);
+    hook_after(K_HEADS_W2, s);
   }
+  hook_before(K_TOPK, s);
   topk_rows<<<dim3(L.chunks, B * K), kTopkThreads, 0, s>>>(lg, V, topk, L.chunks, part, counters,
                                                            topk_ids, topk_logits);
+  hook_after(K_TOPK, s);
   return hipGetLastError();
 }
 

@@ -7,15 +7,32 @@
 
 namespace medusa {
 
+// ---- per-kernel timing hook (medusa_set_kernel_events) -----------------------------------
+constexpr int kKernelCount = 8;
+enum KernelId { K_HEADS_W1 = 0, K_HEADS_W2, K_TOPK, K_TREE_GATHER, K_ATTENTION, K_ATTN_COMBINE,
+                K_ACCEPT, K_NEXT_TOKEN };
+struct EventHook {
+  hipEvent_t before = nullptr, after = nullptr;
+};
+EventHook* event_hooks();   // this thread's hooks, kKernelCount entries
+inline void hook_before(int k, hipStream_t s) {
+  if (event_hooks()[k].before) (void)hipEventRecord(event_hooks()[k].before, s);
+}
+inline void hook_after(int k, hipStream_t s) {
+  if (event_hooks()[k].after) (void)hipEventRecord(event_hooks()[k].after, s);
+}
+
 // ---- heads -------------------------------------------------------------------------------
 struct HeadsWs {
-  size_t r, xfrag, logits, part, counters, total;
+  size_t r, xs, logits, part, counters, total;
   int chunks;
 };
 HeadsWs heads_ws_layout(int B, int hd, long V, int K, int topk);
 hipError_t launch_heads(const void* h, const void* w1, const void* b1, const void* w2, int dtype,
-                        int B, int hd, long V, int K, int topk, float* logits, int32_t* topk_ids,
-                        float* topk_logits, char* ws, hipStream_t s);
+                        int packed, int B, int hd, long V, int K, int topk, float* logits,
+                        int32_t* topk_ids, float* topk_logits, char* ws, hipStream_t s);
+size_t packed_weight_bytes(int K, long rows, int hd);
+hipError_t launch_pack_weights(const void* w, int K, long rows, int hd, void* packed, hipStream_t s);
 
 // ---- tree --------------------------------------------------------------------------------
 hipError_t launch_tree_gather(const int32_t* topk_ids, int K, int topk, const int32_t* root_tokens,

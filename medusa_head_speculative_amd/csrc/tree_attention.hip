@@ -400,9 +400,11 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
   const int W = (T + 63) / 64;
   const float sl2 = scale * 1.4426950408889634f;
   if (dtype == 0) {
+    hook_before(K_ATTENTION, s);
     tree_attn_f32<<<static_cast<unsigned>(static_cast<long>(B) * Hq * T), 64, 0, s>>>(
         static_cast<const float*>(q), static_cast<const float*>(kc), static_cast<const float*>(vc),
         prefix_len, mask, static_cast<float*>(out), lcap, Hq, Hkv, T, W, D, sl2, max_prefix_len);
+    hook_after(K_ATTENTION, s);
     return hipGetLastError();
   }
   AttnArgs a{};
@@ -429,11 +431,16 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
   a.sl2 = sl2;
   a.Lmax = max_prefix_len;
   const unsigned grid = static_cast<unsigned>(((a.nwork + 7) / 8) * 8);
+  hook_before(K_ATTENTION, s);
   if (D == 128) tree_attn_bf16<128><<<grid, 256, 0, s>>>(a);
   else tree_attn_bf16<64><<<grid, 256, 0, s>>>(a);
-  if (P.splits > 1)
+  hook_after(K_ATTENTION, s);
+  if (P.splits > 1) {
+    hook_before(K_ATTN_COMBINE, s);
     tree_attn_combine<uint16_t><<<static_cast<unsigned>(static_cast<long>(B) * Hkv * P.M), D, 0, s>>>(
         a.o_part, a.ml_part, a.out, B, Hq, Hkv, T, P.G, P.M, a.Mpad, P.splits, D);
+    hook_after(K_ATTN_COMBINE, s);
+  }
   return hipGetLastError();
 }
 

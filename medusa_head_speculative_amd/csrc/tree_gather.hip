@@ -28,8 +28,10 @@ hipError_t launch_tree_gather(const int32_t* topk_ids, int K, int topk, const in
                               const int32_t* rank, int32_t* tokens, int32_t* position_ids,
                               hipStream_t s) {
   const long n = static_cast<long>(B) * T;
+  hook_before(K_TREE_GATHER, s);
   tree_gather<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
       topk_ids, K, topk, root_tokens, prefix_len, B, T, depth, rank, tokens, position_ids);
+  hook_after(K_TREE_GATHER, s);
   return hipGetLastError();
 }
 

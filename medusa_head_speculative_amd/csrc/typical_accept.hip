@@ -118,17 +118,61 @@ struct AcceptArgs {
   int32_t* rowarg;        // [B][T]
   unsigned* cnt_row;      // [B][n_int]
   unsigned* cnt_b;        // [B]
-  int32_t* last;          // [B]
   int32_t* best;
   int32_t* accept_len;
+  int32_t* next_token;    // nullable
 };
+
+// Block-wide merge of (statistics, argmax key) in a fixed order: lanes toward lane 0 of each wave,
+// then the waves in order.  The result is valid in thread 0.
+__device__ __forceinline__ void block_merge(RowStat& st, uint64_t& arg, bool greedy, RowStat* s_stat,
+                                            uint64_t* s_arg) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = shfl_down_u64(arg, off);
+    arg = o > arg ? o : arg;
+    if (!greedy) st = stat_merge(st, shfl_down_stat(st, off));
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_stat[w] = st;
+    s_arg[w] = arg;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < kAccThreads / 64; ++i) {
+      st = stat_merge(st, s_stat[i]);
+      arg = s_arg[i] > arg ? s_arg[i] : arg;
+    }
+  }
+}
+
+// argmax (lowest index on ties) of one row, whole block; every thread gets it
+__device__ __forceinline__ uint64_t block_row_argmax(const void* row, int dtype, long V,
+                                                     uint64_t* scratch) {
+  uint64_t arg = 0;
+  for (long i0 = static_cast<long>(threadIdx.x) * kAccPerThread; i0 < V; i0 += kAccChunk) {
+    float x[kAccPerThread];
+    bool valid[kAccPerThread];
+    load8(row, dtype, i0, V, x, valid);
+#pragma unroll
+    for (int e = 0; e < kAccPerThread; ++e)
+      if (valid[e]) {
+        const uint64_t k = sel_key(x[e], static_cast<uint32_t>(i0 + e));
+        arg = k > arg ? k : arg;
+      }
+  }
+  return block_max_u64<kAccThreads>(arg, scratch);
+}
 
 __global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
   __shared__ RowStat s_stat[kAccThreads / 64];
   __shared__ uint64_t s_arg[kAccThreads / 64];
+  __shared__ uint64_t s_scratch[kAccThreads / 64];
   __shared__ int s_last;
   __shared__ RowStat s_row;
   __shared__ uint64_t s_rowarg;
+  __shared__ int32_t s_dec[4096];
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int n = a.internal[r];
   const int esz = a.dtype == 1 ? 2 : 4;
@@ -167,50 +211,33 @@ __global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
       st = RowStat{m, S, A, 0.f};
     }
   }
-  // fixed-order reductions: within the wave toward lane 0, then across waves in wave order
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = shfl_down_u64(arg, off);
-    arg = o > arg ? o : arg;
-    if (!a.greedy) st = stat_merge(st, shfl_down_stat(st, off));
-  }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    s_stat[w] = st;
-    s_arg[w] = arg;
-  }
-  __syncthreads();
-  const long pidx = (static_cast<long>(b) * a.n_int + r) * a.C + c;
+  block_merge(st, arg, a.greedy, s_stat, s_arg);
+  const long prow = (static_cast<long>(b) * a.n_int + r) * a.C;
   if (threadIdx.x == 0) {
-    RowStat t = s_stat[0];
-    uint64_t g = s_arg[0];
-    for (int i = 1; i < kAccThreads / 64; ++i) {
-      t = stat_merge(t, s_stat[i]);
-      g = s_arg[i] > g ? s_arg[i] : g;
-    }
-    a.part_stat[pidx] = t;
-    a.part_arg[pidx] = g;
+    a.part_stat[prow + c] = st;
+    a.part_arg[prow + c] = arg;
     __threadfence();
     s_last = atomicAdd(&a.cnt_row[static_cast<long>(b) * a.n_int + r], 1u) == static_cast<unsigned>(a.C - 1);
   }
   __syncthreads();
   if (!s_last) return;
 
-  // ---- last chunk of this row: merge the partials in chunk order, decide the children ----
+  // ---- last chunk of this row: merge the C partials (fixed order), decide the children ----
   __threadfence();
+  st = RowStat{-INFINITY, 0.f, 0.f, 0.f};
+  arg = 0;
+  for (int i = threadIdx.x; i < a.C; i += kAccThreads) {   // thread t merges t, t+256, ...
+    st = stat_merge(st, a.part_stat[prow + i]);
+    const uint64_t g = a.part_arg[prow + i];
+    arg = g > arg ? g : arg;
+  }
+  __syncthreads();
+  block_merge(st, arg, a.greedy, s_stat, s_arg);
   if (threadIdx.x == 0) {
-    const long p0 = (static_cast<long>(b) * a.n_int + r) * a.C;
-    RowStat t = a.part_stat[p0];
-    uint64_t g = a.part_arg[p0];
-    for (int i = 1; i < a.C; ++i) {
-      t = stat_merge(t, a.part_stat[p0 + i]);
-      const uint64_t gi = a.part_arg[p0 + i];
-      g = gi > g ? gi : g;
-    }
-    s_row = t;
-    s_rowarg = g;
+    s_row = st;
+    s_rowarg = arg;
     a.cnt_row[static_cast<long>(b) * a.n_int + r] = 0u;
-    a.rowarg[static_cast<long>(b) * a.T + n] = static_cast<int32_t>(sel_key_index(g));
+    a.rowarg[static_cast<long>(b) * a.T + n] = static_cast<int32_t>(sel_key_index(arg));
   }
   __syncthreads();
   const int c0 = a.child_ptr[n], c1 = a.child_ptr[n + 1];
@@ -242,73 +269,36 @@ __global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
 
   // ---- last row of this sequence: longest accepted prefix over the paths ----
   __threadfence();
-  __shared__ uint64_t scratch[kAccThreads / 64];
+  for (int i = threadIdx.x; i < a.T; i += kAccThreads) s_dec[i] = a.dec[static_cast<long>(b) * a.T + i];
+  __syncthreads();
   uint64_t bestk = 0;
   for (int p = threadIdx.x; p < a.n_paths; p += kAccThreads) {
     const int32_t* path = a.paths + static_cast<long>(p) * (a.dmax + 1);
     const int len = a.path_len[p];
     int k = 0;
-    while (k < len && a.dec[static_cast<long>(b) * a.T + path[k + 1]]) ++k;
+    while (k < len && s_dec[path[k + 1]]) ++k;
     const uint64_t key = (static_cast<uint64_t>(k) << 32) | (0xffffffffu - static_cast<uint32_t>(p));
     bestk = key > bestk ? key : bestk;
   }
-  bestk = block_max_u64<kAccThreads>(bestk, scratch);
+  bestk = block_max_u64<kAccThreads>(bestk, s_scratch);
+  const int p = static_cast<int>(0xffffffffu - static_cast<uint32_t>(bestk & 0xffffffffu));
+  const int k = static_cast<int>(bestk >> 32);
+  const int last = a.paths[static_cast<long>(p) * (a.dmax + 1) + k];
   if (threadIdx.x == 0) {
-    const int p = static_cast<int>(0xffffffffu - static_cast<uint32_t>(bestk & 0xffffffffu));
-    const int k = static_cast<int>(bestk >> 32);
     a.best[b] = p;
     a.accept_len[b] = k;
-    a.last[b] = a.paths[static_cast<long>(p) * (a.dmax + 1) + k];
     a.cnt_b[b] = 0u;
   }
-}
-
-// next_token[b] = argmax of the row of the last accepted node (lowest id on ties).  If that node
-// is internal its argmax is already known; otherwise the (leaf) row is read here.
-__global__ __launch_bounds__(kAccThreads) void accept_next_token(const void* logits, int dtype,
-                                                                 int T, long V, int C,
-                                                                 const int32_t* child_ptr,
-                                                                 const int32_t* last,
-                                                                 const int32_t* rowarg,
-                                                                 uint64_t* part, unsigned* cnt,
-                                                                 int32_t* next_token) {
-  __shared__ uint64_t scratch[kAccThreads / 64];
-  __shared__ int s_last;
-  const int c = blockIdx.x, b = blockIdx.y;
-  const int n = last[b];
-  if (child_ptr[n + 1] > child_ptr[n]) {
-    if (c == 0 && threadIdx.x == 0) next_token[b] = rowarg[static_cast<long>(b) * T + n];
-    return;
-  }
-  const int esz = dtype == 1 ? 2 : 4;
-  const char* row = static_cast<const char*>(logits) + (static_cast<long>(b) * T + n) * V * esz;
-  const long idx0 = static_cast<long>(c) * kAccChunk + static_cast<long>(threadIdx.x) * kAccPerThread;
-  float x[kAccPerThread];
-  bool valid[kAccPerThread];
-  load8(row, dtype, idx0, V, x, valid);
-  uint64_t arg = 0;
-#pragma unroll
-  for (int e = 0; e < kAccPerThread; ++e)
-    if (valid[e]) {
-      const uint64_t k = sel_key(x[e], static_cast<uint32_t>(idx0 + e));
-      arg = k > arg ? k : arg;
+  if (a.next_token) {
+    // the greedy token after the last accepted node; its argmax is known if it has children
+    if (a.child_ptr[last + 1] > a.child_ptr[last]) {
+      if (threadIdx.x == 0) a.next_token[b] = a.rowarg[static_cast<long>(b) * a.T + last];
+    } else {
+      const char* lrow = static_cast<const char*>(a.logits) + (static_cast<long>(b) * a.T + last) * a.V * esz;
+      const uint64_t g = block_row_argmax(lrow, a.dtype, a.V, s_scratch);
+      if (threadIdx.x == 0) a.next_token[b] = static_cast<int32_t>(sel_key_index(g));
     }
-  arg = block_max_u64<kAccThreads>(arg, scratch);
-  if (threadIdx.x == 0) {
-    part[static_cast<long>(b) * C + c] = arg;
-    __threadfence();
-    s_last = atomicAdd(&cnt[b], 1u) == static_cast<unsigned>(C - 1);
   }
-  __syncthreads();
-  if (!s_last || threadIdx.x != 0) return;
-  __threadfence();
-  uint64_t g = 0;
-  for (int i = 0; i < C; ++i) {
-    const uint64_t v = part[static_cast<long>(b) * C + i];
-    g = v > g ? v : g;
-  }
-  next_token[b] = static_cast<int32_t>(sel_key_index(g));
-  cnt[b] = 0u;
 }
 
 AcceptWs accept_ws_layout(int B, int T, long V, int n_internal) {
@@ -363,15 +353,12 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, lo
   a.rowarg = a.dec + static_cast<size_t>(B) * T;
   a.cnt_row = reinterpret_cast<unsigned*>(ws + L.cnt_row);
   a.cnt_b = reinterpret_cast<unsigned*>(ws + L.cnt_b);
-  a.last = reinterpret_cast<int32_t*>(ws + L.last);
   a.best = best;
   a.accept_len = accept_len;
+  a.next_token = next_token;
+  hook_before(K_ACCEPT, s);
   accept_rows<<<dim3(L.chunks, n_internal, B), kAccThreads, 0, s>>>(a);
-  if (next_token)
-    accept_next_token<<<dim3(L.chunks, B), kAccThreads, 0, s>>>(
-        logits, dtype, T, V, L.chunks, child_ptr, a.last, a.rowarg,
-        reinterpret_cast<uint64_t*>(ws + L.npart), reinterpret_cast<unsigned*>(ws + L.cnt_nt),
-        next_token);
+  hook_after(K_ACCEPT, s);
   return hipGetLastError();
 }
 

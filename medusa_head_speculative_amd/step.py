@@ -32,8 +32,14 @@ class VerifyStep:
             _lib.typical_accept_workspace(B, T, vocab, self.tree.dims["n_internal"]), device)
 
     def heads(self, h, w1, b1, w2, stream=None):
-        _lib.medusa_heads(h, w1, b1, w2, self.topk, self.topk_ids, self.ws_heads, logits=self.logits,
-                          topk_logits=self.topk_logits, stream=stream)
+        """w1/w2 either [K, out, in] tensors or the flat packed tensors of pack_weights."""
+        if w1.dim() == 1:
+            _lib.medusa_heads_packed(h, w1, b1, w2, self.vocab, self.K, self.topk, self.topk_ids,
+                                     self.ws_heads, logits=self.logits,
+                                     topk_logits=self.topk_logits, stream=stream)
+        else:
+            _lib.medusa_heads(h, w1, b1, w2, self.topk, self.topk_ids, self.ws_heads,
+                              logits=self.logits, topk_logits=self.topk_logits, stream=stream)
 
     def build(self, root_tokens, prefix_len, stream=None):
         _lib.build_tree(self.tree, self.topk_ids, root_tokens, prefix_len, self.tokens,

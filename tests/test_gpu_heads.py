@@ -116,3 +116,77 @@ def test_heads_deterministic():
     for x, y in zip(a, b):
         assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
                               y.view(np.uint32) if y.dtype == np.float32 else y)
+
+
+# ---- packed weights (medusa_pack_weights + medusa_heads_packed) ----------------------------
+def _pack_reference(w):
+    """The documented packed order, written out with numpy."""
+    K, rows, hd = w.shape
+    nt = (rows + 15) // 16
+    padded = np.zeros((K, nt * 16, hd), w.dtype)
+    padded[:, :rows] = w
+    # [K][tile][16 rows][hd/32 kb][4 groups][8] -> [K][tile][kb][group][row][8]
+    x = padded.reshape(K, nt, 16, hd // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5)
+    return np.ascontiguousarray(x).reshape(-1)
+
+
+@pytest.mark.parametrize("K,rows,hd", [(1, 16, 32), (2, 37, 64), (3, 1000, 256), (1, 5, 4096)])
+def test_pack_layout(K, rows, hd):
+    import torch
+    m = lib()
+    w = normals((K, rows, hd), 3, 1, 0, 1.0, "bf16")
+    say("pack layout", K, rows, hd)
+    p = m.pack_weights(dev(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(p), _pack_reference(w))
+
+
+def run_heads_packed(m, inp, K, V, topk):
+    import torch
+    B, hd = inp["h"].shape
+    w1p, w2p = m.pack_weights(dev(inp["w1"])), m.pack_weights(dev(inp["w2"]))
+    ws = m.workspace(m.medusa_heads_workspace(B, hd, V, K, topk))
+    logits = torch.full((B, K, V), float("nan"), dtype=torch.float32, device="cuda")
+    ids = torch.full((B, K, topk), -1, dtype=torch.int32, device="cuda")
+    m.medusa_heads_packed(dev(inp["h"]), w1p, dev(inp["b1"]), w2p, V, K, topk, ids, ws, logits=logits)
+    torch.cuda.synchronize()
+    return host(logits), host(ids)
+
+
+@pytest.mark.parametrize("ci", [1, 2, 3, 4])
+def test_heads_packed_full_size(ci):
+    cfg = get_config(ci)
+    m = lib()
+    inp = gen_head_inputs(cfg)
+    _, l64 = oracle.heads(inp["h"], inp["w1"], inp["b1"], inp["w2"], cfg.dtype)
+    say("heads packed full size", cfg.name)
+    lg, ids = run_heads_packed(m, inp, cfg.K, cfg.V, cfg.topk)
+    err = float(np.abs(lg - l64).max())
+    print(f"{cfg.name} packed: max |logit - oracle| = {err:.3e}")
+    assert err <= tol(cfg.dtype)
+    check_topk(ids, l64, cfg.topk)
+
+
+@pytest.mark.parametrize("B,hd,V,K,topk", [(1, 32, 1, 1, 1), (3, 64, 63, 2, 5), (8, 96, 65, 3, 64),
+                                           (2, 128, 257, 8, 10), (5, 4096, 4097, 2, 10)])
+def test_heads_packed_ragged(B, hd, V, K, topk):
+    m = lib()
+    cfg = custom(dtype="bf16", B=B, Hd=hd, V=V, K=K, topk=topk, w_std=1.0 / np.sqrt(hd), seed=B + K)
+    inp = gen_head_inputs(cfg)
+    _, l64 = oracle.heads(inp["h"], inp["w1"], inp["b1"], inp["w2"], "bf16")
+    say("heads packed ragged", B, hd, V, K, topk)
+    lg, ids = run_heads_packed(m, inp, K, V, topk)
+    assert float(np.abs(lg - l64).max()) <= tol("bf16")
+    check_topk(ids, l64, topk)
+
+
+def test_zero_init_heads_packed():
+    hd, V, K, topk = 256, 1000, 3, 8
+    m = lib()
+    lm = normals((V, hd), 78, 1, 2, 0.02, "bf16")
+    h = normals((1, hd), 78, 0, 0, 1.0, "bf16")
+    inp = dict(h=h, w1=np.zeros((K, hd, hd), np.uint16), b1=np.zeros((K, hd), np.uint16),
+               w2=np.ascontiguousarray(np.broadcast_to(lm, (K, V, hd))))
+    say("zero-init heads packed")
+    lg, _ = run_heads_packed(m, inp, K, V, topk)
+    assert [bool(np.array_equal(lg[:, k], lg[:, 0])) for k in range(K)] == [True, True, True]
