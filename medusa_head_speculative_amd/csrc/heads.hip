@@ -315,16 +315,16 @@ __global__ __launch_bounds__(256) void heads_gemv_f32(const float* __restrict__ 
 // the rounds below need no tie handling.  One round picks the best key below the previous
 // winner with a wave-wide max (DPP, no LDS).
 //
-// Grid (C chunks of 4096, R rows).  Phase 1: each wave keeps the k best of its 1024 elements;
-// wave 0 merges the 4 waves' lists into the chunk's k best.  Phase 2: the last work-group of the
-// row to finish (atomic counter) merges the C*k chunk candidates, 1024 at a time, each batch
-// together with the running best list.
+// Two launches, no cross-work-group handoff: topk_chunks (grid C x R) reduces each 2048-element
+// chunk to its k best (each wave its 512 elements, then wave 0 merges the 4 lists);
+// topk_merge (grid R, one wave) merges the C*k candidates of a row, 512 at a time together with
+// the running list.
 constexpr int kTopkThreads = 256;
-constexpr int kTopkPerThread = 16;
-constexpr int kTopkChunk = kTopkThreads * kTopkPerThread;
+constexpr int kTopkPerLane = 8;
+constexpr int kTopkChunk = kTopkThreads * kTopkPerLane;   // 2048
 
-// k rounds over NK keys per lane plus an optional running list (lane t < k holds entry t).
-// Returns the new list in lanes 0..k-1 (lane t: t-th best); other lanes get 0.
+// k rounds over NK keys per lane plus a running list (lane t < k holds entry t).  Returns the
+// new list in lanes 0..k-1 (lane t: t-th best); other lanes get 0.
 template <int NK>
 __device__ __forceinline__ uint64_t wave_select(const uint64_t (&keys)[NK], uint64_t running, int k) {
   const int lane = threadIdx.x & 63;
@@ -341,45 +341,40 @@ __device__ __forceinline__ uint64_t wave_select(const uint64_t (&keys)[NK], uint
   return mine;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restrict__ logits, long V,
-                                                          int k, int C, uint64_t* __restrict__ part,
-                                                          unsigned* __restrict__ counters,
-                                                          int32_t* __restrict__ ids,
-                                                          float* __restrict__ vals) {
+__global__ __launch_bounds__(kTopkThreads) void topk_chunks(const float* __restrict__ logits, long V,
+                                                            int k, int C,
+                                                            uint64_t* __restrict__ part) {
   __shared__ uint64_t s_cand[4][64];
-  __shared__ int s_last;
   const int row = blockIdx.y, c = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* x = logits + static_cast<long>(row) * V;
-  uint64_t keys[kTopkPerThread];
-  const long base = static_cast<long>(c) * kTopkChunk + wave * 1024;
+  uint64_t keys[kTopkPerLane];
+  const long base = static_cast<long>(c) * kTopkChunk + wave * (kTopkChunk / 4);
 #pragma unroll
-  for (int e = 0; e < kTopkPerThread; ++e) {
+  for (int e = 0; e < kTopkPerLane; ++e) {
     const long idx = base + e * 64 + lane;
     keys[e] = idx < V ? sel_key(x[idx], static_cast<uint32_t>(idx)) : 0ull;
   }
   s_cand[wave][lane] = wave_select(keys, 0ull, k);
   __syncthreads();
-  if (wave == 0) {
-    uint64_t k4[4];
+  if (wave != 0) return;
+  uint64_t k4[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) k4[w] = lane < k ? s_cand[w][lane] : 0ull;
-    const uint64_t mine = wave_select(k4, 0ull, k);
-    if (lane < k) part[(static_cast<long>(row) * C + c) * k + lane] = mine;
-    __threadfence();
-    if (lane == 0) s_last = atomicAdd(&counters[row], 1u) == static_cast<unsigned>(C - 1);
-  }
-  __syncthreads();
-  if (!s_last || wave != 0) return;
+  for (int w = 0; w < 4; ++w) k4[w] = lane < k ? s_cand[w][lane] : 0ull;
+  const uint64_t mine = wave_select(k4, 0ull, k);
+  if (lane < k) part[(static_cast<long>(row) * C + c) * k + lane] = mine;
+}
 
-  // ---- phase 2 (one wave): the C*k chunk candidates, 1024 per batch ----
-  __threadfence();
+__global__ __launch_bounds__(64) void topk_merge(const uint64_t* __restrict__ part, int k, int C,
+                                                 int32_t* __restrict__ ids, float* __restrict__ vals) {
+  const int row = blockIdx.x, lane = threadIdx.x;
   const uint64_t* pr = part + static_cast<long>(row) * C * k;
   const long n = static_cast<long>(C) * k;
   uint64_t running = 0;
-  for (long b0 = 0; b0 < n; b0 += 1024) {
+  for (long b0 = 0; b0 < n; b0 += 64 * kTopkPerLane) {
+    uint64_t keys[kTopkPerLane];
 #pragma unroll
-    for (int e = 0; e < kTopkPerThread; ++e) {
+    for (int e = 0; e < kTopkPerLane; ++e) {
       const long i = b0 + e * 64 + lane;
       keys[e] = i < n ? pr[i] : 0ull;
     }
@@ -389,7 +384,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* __restric
     ids[static_cast<long>(row) * k + lane] = static_cast<int32_t>(sel_key_index(running));
     if (vals) vals[static_cast<long>(row) * k + lane] = sel_key_value(running);
   }
-  if (lane == 0) counters[row] = 0u;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -427,10 +421,11 @@ struct PackedVariant {
   int tpw, u, ksplit;
 };
 static const PackedVariant kPackedVariants[] = {
-    {1, 8, 4}, {2, 8, 4}, {1, 8, 1}, {2, 4, 1}, {2, 8, 1}, {4, 4, 1}, {4, 8, 1}, {1, 16, 1}};
+    {1, 8, 4}, {2, 8, 4}, {1, 8, 1}, {2, 4, 1}, {2, 8, 1}, {4, 4, 1}, {4, 8, 1}, {1, 16, 1},
+    {1, 16, 4}, {1, 4, 4}};
 constexpr int kDefaultW1Variant = 0;
-constexpr int kDefaultW2VariantSmallB = 2;   // B <= 2: one tile per wave, 8 blocks in flight
-constexpr int kDefaultW2Variant = 4;         // B > 2: two tiles per wave share the x operand
+constexpr int kDefaultW2VariantSmallB = 2;   // B <= 4: one tile per wave, 8 blocks in flight
+constexpr int kDefaultW2Variant = 4;         // B > 4: two tiles per wave share the x operand
 
 static int variant_from_env(const char* name, int dflt) {
   const char* v = getenv(name);
@@ -455,7 +450,9 @@ static void launch_packed(int variant, const uint16_t* Wp, const uint16_t* x, in
     MEDUSA_PACKED_CASE(4, 2, 8, 1)
     MEDUSA_PACKED_CASE(5, 4, 4, 1)
     MEDUSA_PACKED_CASE(6, 4, 8, 1)
-    default: MEDUSA_PACKED_CASE(7, 1, 16, 1)
+    MEDUSA_PACKED_CASE(7, 1, 16, 1)
+    MEDUSA_PACKED_CASE(8, 1, 16, 4)
+    default: MEDUSA_PACKED_CASE(9, 1, 4, 4)
   }
 #undef MEDUSA_PACKED_CASE
 }
@@ -476,7 +473,7 @@ hipError_t launch_heads(const void* h, const void* w1, const void* b1, const voi
   if (dtype == 1 && packed) {
     static const int v1 = variant_from_env("MEDUSA_W1_VARIANT", kDefaultW1Variant);
     static const int v2_env = variant_from_env("MEDUSA_W2_VARIANT", -1);
-    const int v2 = v2_env >= 0 ? v2_env : (B <= 2 ? kDefaultW2VariantSmallB : kDefaultW2Variant);
+    const int v2 = v2_env >= 0 ? v2_env : (B <= 4 ? kDefaultW2VariantSmallB : kDefaultW2Variant);
     hook_before(K_HEADS_W1, s);
     launch_packed(v1, static_cast<const uint16_t*>(w1), hb, B, e1, s);
     hook_after(K_HEADS_W1, s);
@@ -503,9 +500,10 @@ hipError_t launch_heads(const void* h, const void* w1, const void* b1, const voi
                                                         static_cast<long>(K) * hd, hd, e2);
     hook_after(K_HEADS_W2, s);
   }
+  (void)counters;
   hook_before(K_TOPK, s);
-  topk_rows<<<dim3(L.chunks, B * K), kTopkThreads, 0, s>>>(lg, V, topk, L.chunks, part, counters,
-                                                           topk_ids, topk_logits);
+  topk_chunks<<<dim3(L.chunks, B * K), kTopkThreads, 0, s>>>(lg, V, topk, L.chunks, part);
+  topk_merge<<<B * K, 64, 0, s>>>(part, topk, L.chunks, topk_ids, topk_logits);
   hook_after(K_TOPK, s);
   return hipGetLastError();
 }

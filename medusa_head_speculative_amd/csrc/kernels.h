@@ -56,7 +56,7 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
 
 // ---- typical acceptance ------------------------------------------------------------------
 struct AcceptWs {
-  size_t part, dec, cnt_row, cnt_b, last, npart, cnt_nt, total;
+  size_t part, dec, total;
   int chunks;
 };
 AcceptWs accept_ws_layout(int B, int T, long V, int n_internal);

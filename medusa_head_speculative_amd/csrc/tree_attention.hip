@@ -27,6 +27,7 @@ namespace medusa {
 
 constexpr int kAttnRows = 128;   // query rows per work-group (4 waves x 32)
 constexpr int kKvTile = 64;
+constexpr int kMaxSplits = 16;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 
@@ -53,13 +54,9 @@ __device__ __forceinline__ s16x4_t lds_read_tr(const uint16_t* p) {
       (__attribute__((address_space(3))) s16x4_t*)(p));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16_rne(lo)) | (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
-}
-
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
-  constexpr int KP = D + 8;              // LDS row pitch in elements (272 B for D = 128)
+  constexpr int KP = D + 16;             // LDS row pitch in elements (288 B for D = 128)
   constexpr int NKB = D / 32;            // 32-wide contraction blocks over the head dim
   constexpr int NDB = D / 16;            // 16-wide output blocks over the head dim
   constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
@@ -89,15 +86,18 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
   const int t_end = static_cast<int>((static_cast<long>(split + 1) * ntiles) / a.splits);
   const long kvbase = (static_cast<long>(b) * a.Hkv + kvh) * a.lcap;
 
-  // ---- tree tiles that some row of this work-group can see ----
-  for (int t = tid; t < 64; t += 256) s_active[t] = 0;
-  __syncthreads();
-  for (int p = tid; p < kAttnRows * ntt; p += 256) {
-    const int r = p / ntt, t = p - r * ntt;
-    const int m = qt * kAttnRows + r;
-    if (m < a.M && a.mask[static_cast<long>(m / a.G) * a.W + t] != 0ull) s_active[t] = 1;
+  // ---- tree tiles that some row of this work-group can see (only needed if the K/V range of
+  //      this work-group reaches the tree rows) ----
+  const bool has_tree = t_end > np;
+  if (has_tree) {
+    for (int t = tid; t < 64; t += 256) s_active[t] = 0;
+    __syncthreads();
+    for (int p = tid; p < kAttnRows * ntt; p += 256) {
+      const int r = p / ntt, t = p - r * ntt;
+      const int m = qt * kAttnRows + r;
+      if (m < a.M && a.mask[static_cast<long>(m / a.G) * a.W + t] != 0ull) s_active[t] = 1;
+    }
   }
-  __syncthreads();
 
   // ---- this lane's two query rows (mb = 0, 1) ----
   int node[2];
@@ -157,6 +157,7 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
     }
   };
 
+  if (has_tree) __syncthreads();
   int t = next_active(t_begin);
   if (t < t_end) load_tile(t);
   while (t < t_end) {
@@ -188,48 +189,61 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
       }
     }
 
-    // ---- mask, online softmax (log2 domain), P as the B operand of the second product ----
+    // ---- mask, online softmax (log2 domain), P as the B operand of the second product.
+    //      The running max is raised lazily: p = 2^(s*scale - m) with s*scale <= m + 8, so the
+    //      rescale of O and l (exact either way) runs only when the max grows by more than 8. ----
     const bool is_tree = t >= np;
     int nvalid;
     long row0;
     tile_rows(t, row0, nvalid);
+    const bool full = !is_tree && nvalid == kKvTile;
     uint32_t pb[2][2][4];   // [mb][ks][dword] packed bf16 pairs
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      uint64_t mw = 0;
-      if (is_tree && rvalid[mb]) mw = a.mask[static_cast<long>(node[mb]) * a.W + (t - np)];
       float sv[4][4];
-      float mx = -INFINITY;
+      if (full) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sv[cb][j] = sacc[mb][cb][j];
+      } else {
+        uint64_t mw = ~0ull;
+        if (is_tree) mw = rvalid[mb] ? a.mask[static_cast<long>(node[mb]) * a.W + (t - np)] : 0ull;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int c = cb * 16 + 4 * lg + j;
+            const bool vis = c < nvalid && ((mw >> c) & 1ull);
+            sv[cb][j] = vis ? sacc[mb][cb][j] : -INFINITY;
+          }
+      }
+      float mx = sv[0][0];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = cb * 16 + 4 * lg + j;
-          const bool vis = rvalid[mb] && c < nvalid && (!is_tree || ((mw >> c) & 1ull));
-          sv[cb][j] = vis ? sacc[mb][cb][j] * a.sl2 : -INFINITY;
-          mx = fmaxf(mx, sv[cb][j]);
-        }
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sv[cb][j]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow[mb], mx);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(mrow[mb] - muse);
-      mrow[mb] = mnew;
-      float ps = 0.f;
+      const float mxs = mx * a.sl2;
+      if (mxs > mrow[mb] + 8.f) {                     // raise the reference (rare after the start)
+        const float alpha = exp2f(mrow[mb] - mxs);
+        mrow[mb] = mxs;
+        lsum[mb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) oacc[mb][db][j] *= alpha;
+      }
+      const float nm = mrow[mb] == -INFINITY ? 0.f : -mrow[mb];
       float pr[4][4];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = exp2f(sv[cb][j] - muse);
-          pr[cb][j] = bf16_to_f32(f32_to_bf16_rne(p));
-          ps += pr[cb][j];
+          pr[cb][j] = exp2f(fmaf(sv[cb][j], a.sl2, nm));
+          lsum[mb] += pr[cb][j];
         }
-      lsum[mb] = lsum[mb] * alpha + ps;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) oacc[mb][db][j] *= alpha;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         pb[mb][ks][0] = pack_bf16x2(pr[2 * ks][0], pr[2 * ks][1]);
@@ -249,12 +263,9 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
         const int dcol = db * 16 + 4 * (mm & 3);
         const s16x4_t v0 = lds_read_tr(Vs + crow * KP + dcol);
         const s16x4_t v1 = lds_read_tr(Vs + (crow + 16) * KP + dcol);
-        const uint4 av = make_uint4(
-            static_cast<uint16_t>(v0[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v0[1])) << 16),
-            static_cast<uint16_t>(v0[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(v0[3])) << 16),
-            static_cast<uint16_t>(v1[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v1[1])) << 16),
-            static_cast<uint16_t>(v1[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(v1[3])) << 16));
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, av);
+        typedef __attribute__((ext_vector_type(8))) short s16x8_t;
+        const s16x8_t vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, vv);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           const uint4 bv = make_uint4(pb[mb][ks][0], pb[mb][ks][1], pb[mb][ks][2], pb[mb][ks][3]);
@@ -296,36 +307,71 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
   }
 }
 
-// Merge of the K/V splits, in split order: one block of D threads per query row.
-template <typename OutT>
-__global__ void tree_attn_combine(const float* __restrict__ o_part, const float2* __restrict__ ml,
-                                  OutT* __restrict__ out, int B, int Hq, int Hkv, int T, int G,
-                                  int M, int Mpad, int splits, int D) {
-  const long rowid = blockIdx.x;   // over B * Hkv * M
+// Merge of the K/V splits, in split order.  One wave per query row; every load is issued before
+// any is used (at most kMaxSplits splits).
+template <int D>
+__global__ __launch_bounds__(256) void tree_attn_combine(const float* __restrict__ o_part,
+                                                         const float2* __restrict__ ml,
+                                                         uint16_t* __restrict__ out, int B, int Hq,
+                                                         int Hkv, int T, int G, int M, int Mpad,
+                                                         int splits) {
+  constexpr int PER = D / 64;   // values per lane
+  const long rowid = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);   // over B*Hkv*M
+  if (rowid >= static_cast<long>(B) * Hkv * M) return;
+  const int lane = threadIdx.x & 63;
   const int m = static_cast<int>(rowid % M);
   const long bk = rowid / M;       // b * Hkv + kvh
-  const int d = threadIdx.x;
+  const long stride = static_cast<long>(B) * Hkv * Mpad;
+  float2 v[kMaxSplits];
+  float o[kMaxSplits][PER];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < splits) {
+      const long pr = s * stride + bk * Mpad + m;
+      v[s] = ml[pr];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[s][e] = o_part[pr * D + e * 64 + lane];
+    } else {
+      v[s] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[s][e] = 0.f;
+    }
+  }
   float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, ml[(s * static_cast<long>(B) * Hkv + bk) * Mpad + m].x);
-  float l = 0.f, o = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const long pr = (s * static_cast<long>(B) * Hkv + bk) * Mpad + m;
-    const float2 v = ml[pr];
-    if (v.y == 0.f) continue;
-    const float f = exp2f(v.x - mx);
-    l += v.y * f;
-    o += o_part[pr * D + d] * f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) mx = fmaxf(mx, v[s].x);
+  float l = 0.f, acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (v[s].y == 0.f) continue;
+    const float f = exp2f(v[s].x - mx);
+    l += v[s].y * f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += o[s][e] * f;
   }
   const int b = static_cast<int>(bk / Hkv), kvh = static_cast<int>(bk % Hkv);
   const int node = m / G, hq = kvh * G + m % G;
-  const float r = o / l;
-  OutT* orow = out + ((static_cast<long>(b) * Hq + hq) * T + node) * D;
-  if constexpr (sizeof(OutT) == 2) orow[d] = f32_to_bf16_rne(r);
-  else orow[d] = r;
+  uint16_t* orow = out + ((static_cast<long>(b) * Hq + hq) * T + node) * D;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) orow[e * 64 + lane] = f32_to_bf16_rne(acc[e] / l);
 }
 
-// fp32 path: one wave per (b, q head, node); lanes over the head dim, columns in order with an
-// online softmax.
+// fp32 path: one wave per (b, q head, node).  Columns go 64 at a time: lanes compute one score
+// each (the lane's K row), the wave updates the online softmax, then lanes switch to the head
+// dim and accumulate the chunk's p-weighted V rows (coalesced V loads).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_down(v, off);
+  return __shfl(v, 0);
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
 __global__ __launch_bounds__(64) void tree_attn_f32(const float* __restrict__ q,
                                                     const float* __restrict__ kc,
                                                     const float* __restrict__ vc,
@@ -333,6 +379,8 @@ __global__ __launch_bounds__(64) void tree_attn_f32(const float* __restrict__ q,
                                                     const uint64_t* __restrict__ mask, float* out,
                                                     long lcap, int Hq, int Hkv, int T, int W,
                                                     int D, float sl2, int Lmax) {
+  __shared__ float s_q[128];
+  __shared__ float s_p[64];
   const long u = blockIdx.x;
   const int i = static_cast<int>(u % T);
   const int hq = static_cast<int>((u / T) % Hq);
@@ -342,25 +390,49 @@ __global__ __launch_bounds__(64) void tree_attn_f32(const float* __restrict__ q,
   const int L = min(max(prefix_len[b], 0), Lmax);
   const long base = (static_cast<long>(b) * Hkv + g) * lcap;
   const float* qr = q + u * D;
-  float q0 = lane < D ? qr[lane] : 0.f, q1 = lane + 64 < D ? qr[lane + 64] : 0.f;
+  for (int d = lane; d < D; d += 64) s_q[d] = qr[d];
+  __syncthreads();
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (long j = 0; j < static_cast<long>(L) + T; ++j) {
-    if (j >= L) {
+  const long ncols = static_cast<long>(L) + T;
+  for (long c0 = 0; c0 < ncols; c0 += 64) {
+    const long j = c0 + lane;
+    bool vis = j < ncols;
+    if (vis && j >= L) {
       const int t = static_cast<int>(j - L);
-      if (!((mask[static_cast<long>(i) * W + t / 64] >> (t % 64)) & 1ull)) continue;
+      vis = (mask[static_cast<long>(i) * W + t / 64] >> (t % 64)) & 1ull;
     }
-    const float* kr = kc + (base + j) * D;
-    const float* vr = vc + (base + j) * D;
-    float s = (lane < D ? q0 * kr[lane] : 0.f) + (lane + 64 < D ? q1 * kr[lane + 64] : 0.f);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    s *= sl2;
-    const float mnew = fmaxf(m, s);
-    const float alpha = exp2f(m - mnew), p = exp2f(s - mnew);
-    l = l * alpha + p;
-    o0 = o0 * alpha + (lane < D ? p * vr[lane] : 0.f);
-    o1 = o1 * alpha + (lane + 64 < D ? p * vr[lane + 64] : 0.f);
+    float s = -INFINITY;
+    if (vis) {
+      const float4* kr = reinterpret_cast<const float4*>(kc + (base + j) * D);
+      float acc = 0.f;
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const float4 kv = kr[d4];
+        acc = fmaf(s_q[4 * d4], kv.x, acc);
+        acc = fmaf(s_q[4 * d4 + 1], kv.y, acc);
+        acc = fmaf(s_q[4 * d4 + 2], kv.z, acc);
+        acc = fmaf(s_q[4 * d4 + 3], kv.w, acc);
+      }
+      s = acc * sl2;
+    }
+    const float mnew = fmaxf(m, wave_max_f32(s));
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    const float p = vis ? exp2f(s - muse) : 0.f;
+    const float alpha = exp2f(m - muse);
+    l = l * alpha + wave_sum_f32(p);
     m = mnew;
+    s_p[lane] = p;
+    __syncthreads();
+    o0 *= alpha;
+    o1 *= alpha;
+    const int nc = static_cast<int>(min(static_cast<long>(64), ncols - c0));
+    for (int cc = 0; cc < nc; ++cc) {
+      const float pc = s_p[cc];
+      if (pc == 0.f) continue;
+      const float* vr = vc + (base + c0 + cc) * D;
+      if (lane < D) o0 = fmaf(pc, vr[lane], o0);
+      if (lane + 64 < D) o1 = fmaf(pc, vr[lane + 64], o1);
+    }
+    __syncthreads();
   }
   float* orow = out + u * D;
   if (lane < D) orow[lane] = o0 / l;
@@ -376,9 +448,12 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
   if (dtype == 1) {
     const long units = static_cast<long>(B) * Hkv * p.qtiles;
     const int ntiles = (max_prefix_len + kKvTile - 1) / kKvTile + (T + kKvTile - 1) / kKvTile;
+    // occupancy is one work-group per CU: split the K/V range so the grid is one wave of
+    // work-groups, each with at least two tiles
     if (units < 256) {
-      long s = (384 + units - 1) / units;
+      long s = 256 / units;
       s = s < ntiles / 2 ? s : ntiles / 2;
+      s = s < kMaxSplits ? s : kMaxSplits;
       p.splits = s < 1 ? 1 : static_cast<int>(s);
     }
   }
@@ -437,8 +512,13 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
   hook_after(K_ATTENTION, s);
   if (P.splits > 1) {
     hook_before(K_ATTN_COMBINE, s);
-    tree_attn_combine<uint16_t><<<static_cast<unsigned>(static_cast<long>(B) * Hkv * P.M), D, 0, s>>>(
-        a.o_part, a.ml_part, a.out, B, Hq, Hkv, T, P.G, P.M, a.Mpad, P.splits, D);
+    const unsigned cgrid = static_cast<unsigned>((static_cast<long>(B) * Hkv * P.M + 3) / 4);
+    if (D == 128)
+      tree_attn_combine<128><<<cgrid, 256, 0, s>>>(a.o_part, a.ml_part, a.out, B, Hq, Hkv, T, P.G,
+                                                   P.M, a.Mpad, P.splits);
+    else
+      tree_attn_combine<64><<<cgrid, 256, 0, s>>>(a.o_part, a.ml_part, a.out, B, Hq, Hkv, T, P.G,
+                                                  P.M, a.Mpad, P.splits);
     hook_after(K_ATTN_COMBINE, s);
   }
   return hipGetLastError();

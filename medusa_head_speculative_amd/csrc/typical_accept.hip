@@ -116,8 +116,6 @@ struct AcceptArgs {
   uint64_t* part_arg;     // [B][n_int][C]
   int32_t* dec;           // [B][T]
   int32_t* rowarg;        // [B][T]
-  unsigned* cnt_row;      // [B][n_int]
-  unsigned* cnt_b;        // [B]
   int32_t* best;
   int32_t* accept_len;
   int32_t* next_token;    // nullable
@@ -147,42 +145,20 @@ __device__ __forceinline__ void block_merge(RowStat& st, uint64_t& arg, bool gre
   }
 }
 
-// argmax (lowest index on ties) of one row, whole block; every thread gets it
-__device__ __forceinline__ uint64_t block_row_argmax(const void* row, int dtype, long V,
-                                                     uint64_t* scratch) {
-  uint64_t arg = 0;
-  for (long i0 = static_cast<long>(threadIdx.x) * kAccPerThread; i0 < V; i0 += kAccChunk) {
-    float x[kAccPerThread];
-    bool valid[kAccPerThread];
-    load8(row, dtype, i0, V, x, valid);
-#pragma unroll
-    for (int e = 0; e < kAccPerThread; ++e)
-      if (valid[e]) {
-        const uint64_t k = sel_key(x[e], static_cast<uint32_t>(i0 + e));
-        arg = k > arg ? k : arg;
-      }
-  }
-  return block_max_u64<kAccThreads>(arg, scratch);
-}
-
-__global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
+// Kernel 1, grid (C, n_int, B): statistics and argmax of one 2048-element chunk of an internal
+// row, written to the partial arrays.  No cross-work-group synchronisation: a fence per
+// work-group serialises on this GPU, so the merge is a separate launch.
+__global__ __launch_bounds__(kAccThreads) void accept_chunks(AcceptArgs a) {
   __shared__ RowStat s_stat[kAccThreads / 64];
   __shared__ uint64_t s_arg[kAccThreads / 64];
-  __shared__ uint64_t s_scratch[kAccThreads / 64];
-  __shared__ int s_last;
-  __shared__ RowStat s_row;
-  __shared__ uint64_t s_rowarg;
-  __shared__ int32_t s_dec[4096];
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int n = a.internal[r];
   const int esz = a.dtype == 1 ? 2 : 4;
   const char* row = static_cast<const char*>(a.logits) + (static_cast<long>(b) * a.T + n) * a.V * esz;
   const long idx0 = static_cast<long>(c) * kAccChunk + static_cast<long>(threadIdx.x) * kAccPerThread;
-
   float x[kAccPerThread];
   bool valid[kAccPerThread];
   load8(row, a.dtype, idx0, a.V, x, valid);
-
   uint64_t arg = 0;
 #pragma unroll
   for (int e = 0; e < kAccPerThread; ++e)
@@ -212,64 +188,96 @@ __global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
     }
   }
   block_merge(st, arg, a.greedy, s_stat, s_arg);
-  const long prow = (static_cast<long>(b) * a.n_int + r) * a.C;
   if (threadIdx.x == 0) {
-    a.part_stat[prow + c] = st;
-    a.part_arg[prow + c] = arg;
-    __threadfence();
-    s_last = atomicAdd(&a.cnt_row[static_cast<long>(b) * a.n_int + r], 1u) == static_cast<unsigned>(a.C - 1);
+    const long pidx = (static_cast<long>(b) * a.n_int + r) * a.C + c;
+    a.part_stat[pidx] = st;
+    a.part_arg[pidx] = arg;
   }
-  __syncthreads();
-  if (!s_last) return;
+}
 
-  // ---- last chunk of this row: merge the C partials (fixed order), decide the children ----
-  __threadfence();
-  st = RowStat{-INFINITY, 0.f, 0.f, 0.f};
-  arg = 0;
+// Kernel 2, grid (n_int, B): merges one row's C partials in chunk order (fixed tree), then
+// decides the row's children.  The children's tokens and logits are fetched while the partials
+// load.
+__global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
+  __shared__ RowStat s_stat[kAccThreads / 64];
+  __shared__ uint64_t s_arg[kAccThreads / 64];
+  __shared__ RowStat s_row;
+  __shared__ uint64_t s_rowarg;
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int n = a.internal[r];
+  const int esz = a.dtype == 1 ? 2 : 4;
+  const char* row = static_cast<const char*>(a.logits) + (static_cast<long>(b) * a.T + n) * a.V * esz;
+  const int c0 = a.child_ptr[n], nchild = a.child_ptr[n + 1] - c0;   // at most 64 children
+  int child = -1, tok = -1;
+  float ltok = 0.f;
+  if (threadIdx.x < nchild) {
+    child = a.child_idx[c0 + threadIdx.x];
+    tok = a.tokens[static_cast<long>(b) * a.T + child];
+    if (tok >= 0 && tok < a.V)
+      ltok = a.dtype == 1 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[tok])
+                          : reinterpret_cast<const float*>(row)[tok];
+  }
+  const long prow = (static_cast<long>(b) * a.n_int + r) * a.C;
+  RowStat st{-INFINITY, 0.f, 0.f, 0.f};
+  uint64_t arg = 0;
   for (int i = threadIdx.x; i < a.C; i += kAccThreads) {   // thread t merges t, t+256, ...
     st = stat_merge(st, a.part_stat[prow + i]);
     const uint64_t g = a.part_arg[prow + i];
     arg = g > arg ? g : arg;
   }
-  __syncthreads();
   block_merge(st, arg, a.greedy, s_stat, s_arg);
   if (threadIdx.x == 0) {
     s_row = st;
     s_rowarg = arg;
-    a.cnt_row[static_cast<long>(b) * a.n_int + r] = 0u;
     a.rowarg[static_cast<long>(b) * a.T + n] = static_cast<int32_t>(sel_key_index(arg));
   }
   __syncthreads();
-  const int c0 = a.child_ptr[n], c1 = a.child_ptr[n + 1];
-  for (int ci = c0 + threadIdx.x; ci < c1; ci += kAccThreads) {
-    const int child = a.child_idx[ci];
-    const int tok = a.tokens[static_cast<long>(b) * a.T + child];
+  if (threadIdx.x < nchild) {
     int acc;
     if (tok < 0 || tok >= a.V) {
       acc = 0;                               // not a vocab id: never accepted, never read
     } else if (a.greedy) {
       acc = static_cast<uint32_t>(tok) == sel_key_index(s_rowarg);
     } else {
-      const float l = a.dtype == 1 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[tok])
-                                   : reinterpret_cast<const float*>(row)[tok];
       const float log2S = log2f(s_row.S);
       const float ln2 = 0.69314718055994531f;
-      const float lnp = ln2 * (l * a.y_scale - s_row.m - log2S);
+      const float lnp = ln2 * (ltok * a.y_scale - s_row.m - log2S);
       const float H = ln2 * (log2S - s_row.A / s_row.S);
       const float lnthr = fminf(a.ln_eps, a.ln_delta - H);
       acc = lnp > lnthr;
     }
     a.dec[static_cast<long>(b) * a.T + child] = acc;
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&a.cnt_b[b], 1u) == static_cast<unsigned>(a.n_int - 1);
-  __syncthreads();
-  if (!s_last) return;
+}
 
-  // ---- last row of this sequence: longest accepted prefix over the paths ----
-  __threadfence();
-  for (int i = threadIdx.x; i < a.T; i += kAccThreads) s_dec[i] = a.dec[static_cast<long>(b) * a.T + i];
+// argmax (lowest index on ties) of one row, whole block, 4 loads in flight per thread
+__device__ __forceinline__ uint64_t block_row_argmax(const void* row, int dtype, long V,
+                                                     uint64_t* scratch) {
+  uint64_t arg = 0;
+  for (long j0 = static_cast<long>(threadIdx.x) * kAccPerThread; j0 < V; j0 += 4L * kAccChunk) {
+    float x[4][kAccPerThread];
+    bool valid[4][kAccPerThread];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8(row, dtype, j0 + u * kAccChunk, V, x[u], valid[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < kAccPerThread; ++e)
+        if (valid[u][e]) {
+          const uint64_t k = sel_key(x[u][e], static_cast<uint32_t>(j0 + u * kAccChunk + e));
+          arg = k > arg ? k : arg;
+        }
+  }
+  return block_max_u64<kAccThreads>(arg, scratch);
+}
+
+// Kernel 2, grid (B): the longest accepted prefix over the paths, and the next token.
+__global__ __launch_bounds__(kAccThreads) void accept_paths(AcceptArgs a) {
+  __shared__ uint64_t s_scratch[kAccThreads / 64];
+  __shared__ int32_t s_dec[4096];
+  const int b = blockIdx.x;
+  s_dec[0] = 1;
+  for (int i = 1 + threadIdx.x; i < a.T; i += kAccThreads) s_dec[i] = a.dec[static_cast<long>(b) * a.T + i];
   __syncthreads();
   uint64_t bestk = 0;
   for (int p = threadIdx.x; p < a.n_paths; p += kAccThreads) {
@@ -287,17 +295,16 @@ __global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
   if (threadIdx.x == 0) {
     a.best[b] = p;
     a.accept_len[b] = k;
-    a.cnt_b[b] = 0u;
   }
-  if (a.next_token) {
-    // the greedy token after the last accepted node; its argmax is known if it has children
-    if (a.child_ptr[last + 1] > a.child_ptr[last]) {
-      if (threadIdx.x == 0) a.next_token[b] = a.rowarg[static_cast<long>(b) * a.T + last];
-    } else {
-      const char* lrow = static_cast<const char*>(a.logits) + (static_cast<long>(b) * a.T + last) * a.V * esz;
-      const uint64_t g = block_row_argmax(lrow, a.dtype, a.V, s_scratch);
-      if (threadIdx.x == 0) a.next_token[b] = static_cast<int32_t>(sel_key_index(g));
-    }
+  if (!a.next_token) return;
+  // the greedy token after the last accepted node; its argmax is known if it has children
+  if (a.child_ptr[last + 1] > a.child_ptr[last]) {
+    if (threadIdx.x == 0) a.next_token[b] = a.rowarg[static_cast<long>(b) * a.T + last];
+  } else {
+    const int esz = a.dtype == 1 ? 2 : 4;
+    const char* lrow = static_cast<const char*>(a.logits) + (static_cast<long>(b) * a.T + last) * a.V * esz;
+    const uint64_t g = block_row_argmax(lrow, a.dtype, a.V, s_scratch);
+    if (threadIdx.x == 0) a.next_token[b] = static_cast<int32_t>(sel_key_index(g));
   }
 }
 
@@ -309,11 +316,6 @@ AcceptWs accept_ws_layout(int B, int T, long V, int n_internal) {
   w.chunks = static_cast<int>(C);
   w.part = take((sizeof(RowStat) + sizeof(uint64_t)) * static_cast<size_t>(B) * n_internal * C);
   w.dec = take(sizeof(int32_t) * static_cast<size_t>(B) * T * 2);   // decisions + row argmax
-  w.cnt_row = take(sizeof(unsigned) * static_cast<size_t>(B) * n_internal);
-  w.cnt_b = take(sizeof(unsigned) * B);
-  w.last = take(sizeof(int32_t) * B);
-  w.npart = take(sizeof(uint64_t) * static_cast<size_t>(B) * C);
-  w.cnt_nt = take(sizeof(unsigned) * B);
   w.total = off;
   return w;
 }
@@ -351,13 +353,13 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, lo
   a.part_arg = reinterpret_cast<uint64_t*>(ws + L.part + sizeof(RowStat) * nstat);
   a.dec = reinterpret_cast<int32_t*>(ws + L.dec);
   a.rowarg = a.dec + static_cast<size_t>(B) * T;
-  a.cnt_row = reinterpret_cast<unsigned*>(ws + L.cnt_row);
-  a.cnt_b = reinterpret_cast<unsigned*>(ws + L.cnt_b);
   a.best = best;
   a.accept_len = accept_len;
   a.next_token = next_token;
   hook_before(K_ACCEPT, s);
-  accept_rows<<<dim3(L.chunks, n_internal, B), kAccThreads, 0, s>>>(a);
+  accept_chunks<<<dim3(L.chunks, n_internal, B), kAccThreads, 0, s>>>(a);
+  accept_rows<<<dim3(n_internal, B), kAccThreads, 0, s>>>(a);
+  accept_paths<<<B, kAccThreads, 0, s>>>(a);
   hook_after(K_ACCEPT, s);
   return hipGetLastError();
 }
