@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--temperature", type=float, default=None)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time spent timing the oracle (0 disables it)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 256 MiB device copy 3x (untimed), the reference kernel "
+                        "for scaling hardware byte counters")
     return p.parse_args()
 
 
@@ -239,6 +242,14 @@ def main():
                 "kernel": "heads_gemv_packed (vocab projection W2 of all heads, one launch)"
                           if cfg.dtype == "bf16" else "heads_gemv_f32 (vocab projection W2)",
                 "alg_bytes_per_launch": w2_bytes, "avg_launch_ms": round(w2_ms, 5)}
+
+    if args.copy_calibration:
+        src = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_seconds > 0:

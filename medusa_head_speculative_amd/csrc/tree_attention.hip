@@ -54,15 +54,56 @@ __device__ __forceinline__ s16x4_t lds_read_tr(const uint16_t* p) {
       (__attribute__((address_space(3))) s16x4_t*)(p));
 }
 
+// LDS tile layout: 64 K (or V) rows of D bf16, rows back to back; the 16-byte chunks of a row are
+// permuted by an XOR with a row-dependent slot key, so that both operand reads below are free of
+// bank conflicts: the K reads (16 rows, one chunk) and the transposed V reads (4 consecutive rows,
+// 2 chunks).  The direct global->LDS loads write 64 consecutive 16-byte slots per wave
+// instruction, so the permutation is applied on the global side: the lane that fills slot s of
+// row r loads chunk s ^ key(r).
 template <int D>
-__global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
-  constexpr int KP = D + 16;             // LDS row pitch in elements (288 B for D = 128)
+__device__ __forceinline__ int slot_key(int r) {
+  if constexpr (D == 128) {
+    const int q = r & 15;
+    return ((q & 3) << 1) | ((q >> 2) & 1) | (q & 8);
+  } else {
+    return (r >> 1) & 7;
+  }
+}
+template <int D>
+__device__ __forceinline__ int tile_elem(int r, int c) {   // element offset of (row r, chunk c)
+  return r * D + ((c ^ slot_key<D>(r)) << 3);
+}
+
+// Async loads of one 64-row K/V tile straight into LDS (no registers).  Rows past nvalid repeat
+// the last valid row: finite data whose scores the mask removes.
+template <int D>
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kc,
+                                           const uint16_t* __restrict__ vc, long rowbase,
+                                           int nvalid, uint16_t* Kd, uint16_t* Vd, int wave,
+                                           int lane) {
+  constexpr int SLOTS = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / SLOTS;              // rows per wave instruction
+  constexpr int INST = kKvTile / RPI / 4;      // instructions per wave per matrix
+#pragma unroll
+  for (int u = 0; u < INST; ++u) {
+    const int rbase = (wave * INST + u) * RPI;
+    const int r = rbase + lane / SLOTS;
+    const int c = (lane % SLOTS) ^ slot_key<D>(r);
+    const long goff = (rowbase + min(r, nvalid - 1)) * D + c * 8;
+    __builtin_amdgcn_global_load_lds(kc + goff, (__attribute__((address_space(3))) void*)(Kd + rbase * D), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vc + goff, (__attribute__((address_space(3))) void*)(Vd + rbase * D), 16, 0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
   constexpr int NKB = D / 32;            // 32-wide contraction blocks over the head dim
   constexpr int NDB = D / 16;            // 16-wide output blocks over the head dim
-  constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
-  constexpr int CPT = kKvTile * CPR / 256;  // chunks per thread per tile
-  __shared__ __align__(16) uint16_t Ks[kKvTile * KP];
-  __shared__ __align__(16) uint16_t Vs[kKvTile * KP];
+  constexpr int TILE = kKvTile * D;      // elements per K (or V) tile
+  __shared__ __align__(16) uint16_t K0[TILE];
+  __shared__ __align__(16) uint16_t V0[TILE];
+  __shared__ __align__(16) uint16_t K1[TILE];
+  __shared__ __align__(16) uint16_t V1[TILE];
   __shared__ int s_active[64];
 
   // ---- work item; consecutive logical items (query tiles of one K/V range) share an XCD ----
@@ -97,6 +138,28 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
       const int m = qt * kAttnRows + r;
       if (m < a.M && a.mask[static_cast<long>(m / a.G) * a.W + t] != 0ull) s_active[t] = 1;
     }
+    __syncthreads();
+  }
+  auto next_active = [&](int t) {
+    while (t < t_end && t >= np && !s_active[t - np]) ++t;
+    return t;
+  };
+  auto tile_rows = [&](int t, long& row0, int& nvalid) {   // first cache row, valid rows
+    if (t < np) {
+      row0 = static_cast<long>(t) * kKvTile;
+      nvalid = min(kKvTile, L - t * kKvTile);
+    } else {
+      row0 = L + static_cast<long>(t - np) * kKvTile;
+      nvalid = min(kKvTile, a.T - (t - np) * kKvTile);
+    }
+  };
+
+  int t = next_active(t_begin);
+  if (t < t_end) {
+    long row0;
+    int nvalid;
+    tile_rows(t, row0, nvalid);
+    issue_tile<D>(a.kc, a.vc, kvbase + row0, nvalid, K0, V0, wave, lane);
   }
 
   // ---- this lane's two query rows (mb = 0, 1) ----
@@ -123,57 +186,30 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto next_active = [&](int t) {
-    while (t < t_end && t >= np && !s_active[t - np]) ++t;
-    return t;
-  };
-  // first cache row and number of valid rows of tile t
-  auto tile_rows = [&](int t, long& row0, int& nvalid) {
-    if (t < np) {
-      row0 = static_cast<long>(t) * kKvTile;
-      nvalid = min(kKvTile, L - t * kKvTile);
-    } else {
-      row0 = L + static_cast<long>(t - np) * kKvTile;
-      nvalid = min(kKvTile, a.T - (t - np) * kKvTile);
-    }
-  };
-  uint4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int t) {
+  // One pipeline step: wait for tile t in (Kc, Vc), start tile tn into (Kn, Vn), compute tile t.
+  auto step = [&](const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of tile t has landed
+    __syncthreads();                                    // everyone's part; the other buffer is free
+    const bool is_tree = t >= np;
     long row0;
     int nvalid;
     tile_rows(t, row0, nvalid);
+    const bool full = !is_tree && nvalid == kKvTile;
+    uint64_t mw[2] = {~0ull, ~0ull};
+    if (is_tree) {
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int q = tid + 256 * u;
-      const int r = q / CPR, c8 = q - r * CPR;
-      if (r < nvalid) {
-        const long off = (kvbase + row0 + r) * D + c8 * 8;
-        kreg[u] = *reinterpret_cast<const uint4*>(a.kc + off);
-        vreg[u] = *reinterpret_cast<const uint4*>(a.vc + off);
-      } else {
-        kreg[u] = make_uint4(0, 0, 0, 0);
-        vreg[u] = make_uint4(0, 0, 0, 0);
-      }
+      for (int mb = 0; mb < 2; ++mb)
+        mw[mb] = rvalid[mb] ? a.mask[static_cast<long>(node[mb]) * a.W + (t - np)] : 0ull;
     }
-  };
-
-  if (has_tree) __syncthreads();
-  int t = next_active(t_begin);
-  if (t < t_end) load_tile(t);
-  while (t < t_end) {
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int q = tid + 256 * u;
-      const int r = q / CPR, c8 = q - r * CPR;
-      *reinterpret_cast<uint4*>(Ks + r * KP + c8 * 8) = kreg[u];
-      *reinterpret_cast<uint4*>(Vs + r * KP + c8 * 8) = vreg[u];
-    }
-    __syncthreads();
     const int tn = next_active(t + 1);
-    if (tn < t_end) load_tile(tn);
+    if (tn < t_end) {
+      long nrow0;
+      int nnvalid;
+      tile_rows(tn, nrow0, nnvalid);
+      issue_tile<D>(a.kc, a.vc, kvbase + nrow0, nnvalid, Kn, Vn, wave, lane);
+    }
 
-    // ---- scores S^T = K Q^T for this tile ----
+    // ---- scores S^T = K Q^T ----
     f32x4_t sacc[2][4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -183,7 +219,7 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
     for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8_t kf = lds_read16(Ks + (cb * 16 + mm) * KP + kb * 32 + 8 * lg);
+        const bf16x8_t kf = lds_read16(Kc + tile_elem<D>(cb * 16 + mm, kb * 4 + lg));
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) sacc[mb][cb] = mfma16x16x32(kf, qf[mb][kb], sacc[mb][cb]);
       }
@@ -192,32 +228,18 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
     // ---- mask, online softmax (log2 domain), P as the B operand of the second product.
     //      The running max is raised lazily: p = 2^(s*scale - m) with s*scale <= m + 8, so the
     //      rescale of O and l (exact either way) runs only when the max grows by more than 8. ----
-    const bool is_tree = t >= np;
-    int nvalid;
-    long row0;
-    tile_rows(t, row0, nvalid);
-    const bool full = !is_tree && nvalid == kKvTile;
     uint32_t pb[2][2][4];   // [mb][ks][dword] packed bf16 pairs
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float sv[4][4];
-      if (full) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) sv[cb][j] = sacc[mb][cb][j];
-      } else {
-        uint64_t mw = ~0ull;
-        if (is_tree) mw = rvalid[mb] ? a.mask[static_cast<long>(node[mb]) * a.W + (t - np)] : 0ull;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int c = cb * 16 + 4 * lg + j;
-            const bool vis = c < nvalid && ((mw >> c) & 1ull);
-            sv[cb][j] = vis ? sacc[mb][cb][j] : -INFINITY;
-          }
-      }
+        for (int j = 0; j < 4; ++j) {
+          const int c = cb * 16 + 4 * lg + j;
+          const bool vis = full || (c < nvalid && ((mw[mb] >> c) & 1ull));
+          sv[cb][j] = vis ? sacc[mb][cb][j] : -INFINITY;
+        }
       float mx = sv[0][0];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
@@ -260,9 +282,10 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int crow = ks * 32 + 4 * lg + (mm >> 2);
-        const int dcol = db * 16 + 4 * (mm & 3);
-        const s16x4_t v0 = lds_read_tr(Vs + crow * KP + dcol);
-        const s16x4_t v1 = lds_read_tr(Vs + (crow + 16) * KP + dcol);
+        const int chunk = db * 2 + ((mm & 3) >> 1);
+        const int half = (mm & 1) * 4;
+        const s16x4_t v0 = lds_read_tr(Vc + tile_elem<D>(crow, chunk) + half);
+        const s16x4_t v1 = lds_read_tr(Vc + tile_elem<D>(crow + 16, chunk) + half);
         typedef __attribute__((ext_vector_type(8))) short s16x8_t;
         const s16x8_t vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         const bf16x8_t va = __builtin_bit_cast(bf16x8_t, vv);
@@ -274,6 +297,12 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
       }
     }
     t = tn;
+  };
+
+  while (t < t_end) {
+    step(K0, V0, K1, V1);
+    if (t >= t_end) break;
+    step(K1, V1, K0, V0);
   }
 
   // ---- finish: full row sums, then the output or this split's partial ----
