@@ -9,7 +9,10 @@ a 1024-token prefix, bf16, temperature 0.7).
 
 Prints one JSON line: steps/s, the roofline of the dominant kernel (the heads' vocab
 projection, timed per launch with HIP events recorded around it on its own stream), per-kernel
-timings, accepted tokens/s, and the fp64 CPU oracle timed on a bounded sample of the same step.
+timings with their HBM (and, for attention, matrix-core) fractions, the per-step median and
+p10/p90 back to back and with the last-level cache flushed before every step, a streaming-read
+ceiling measured in the same run, accepted tokens/s, and the fp64 CPU oracle timed on a bounded
+sample of the same step.
 """
 
 import argparse
@@ -25,6 +28,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix cores
+FP32_VALU_PEAK_TFLOPS = 157.3    # fp32 vector ALUs
+MALL_FLUSH_BYTES = 1 << 30       # written before each cold step: 4x the 256 MB last-level cache
+CEILING_BYTES = 4 << 30          # buffer read by the streaming-read ceiling kernel
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "heads_w2_vicuna7b_traffic.json")
 
 
@@ -55,6 +62,13 @@ def kernel_bytes(cfg, T, n_int):
         "attention": 2 * B * cfg.Hkv * (cfg.L + T) * cfg.D * s + 2 * B * cfg.Hq * T * cfg.D * s,
         "accept": B * n_int * V * s,
     }
+
+
+def attention_flops(cfg, T, mask):
+    """Algorithmic flops of one tree_attention call: 2 flops per multiply-add of QK^T and of PV
+    over the visible columns only (every prefix column, plus each node's ancestors-or-self)."""
+    anc = int(np.unpackbits(np.ascontiguousarray(mask).view(np.uint8)).sum())
+    return 4 * cfg.D * cfg.B * cfg.Hq * (T * cfg.L + anc), anc
 
 
 def source_digest(path):
@@ -218,6 +232,54 @@ def main():
             ent["hbm_frac"] = round(kb[k] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         kernels[k] = ent
 
+    # ---- per-step distribution, back to back (warm) and with the 256 MB MALL flushed by a
+    #      1 GiB write before every step (cold; the flush is outside the step's events) ----
+    def per_step(n, flush=None):
+        ev = make_events(n)
+        for i in range(n):
+            if flush is not None:
+                flush.fill_(i & 0x7F)
+            ev[i][0].record(stream)
+            run(temperature)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+        return {"median_ms": round(float(np.median(t)), 5),
+                "p10_ms": round(float(np.percentile(t, 10)), 5),
+                "p90_ms": round(float(np.percentile(t, 90)), 5), "steps": n}
+
+    nd = max(10, min(args.steps, 100))
+    warm = per_step(nd)
+    flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    cold = per_step(nd, flush)
+    del flush
+
+    # ---- measured streaming-read ceiling: the library's plain read kernel over 4 GiB ----
+    buf = torch.zeros(CEILING_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    cev = make_events(10)
+    for _ in range(2):
+        m.stream_read(buf, sink)
+    for e0, e1 in cev:
+        e0.record(stream)
+        m.stream_read(buf, sink)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ceiling_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in cev]))
+    ceiling_gbs = CEILING_BYTES / (ceiling_ms * 1e-3) / 1e9
+    del buf, sink
+    for ent in kernels.values():
+        if "GB/s" in ent:
+            ent["ceiling_frac"] = round(ent["GB/s"] / ceiling_gbs, 4)
+    flops, anc = attention_flops(cfg, T, step.tree.mask.cpu().numpy())
+    att = kernels["attention"]
+    att["alg_flops"] = flops
+    att["TFLOP/s"] = round(flops / (att["ms"] * 1e-3) / 1e12, 2)
+    if cfg.dtype == "bf16":
+        att["mfma_frac"] = round(att["TFLOP/s"] / MFMA_BF16_PEAK_TFLOPS, 4)
+    else:
+        att["valu_frac"] = round(att["TFLOP/s"] / FP32_VALU_PEAK_TFLOPS, 4)
+
     # greedy (temperature 0) for context: shorter run
     t0g = None
     if cfg.temps[0] == 0.0 and temperature != 0.0:
@@ -241,7 +303,9 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(),
                 "kernel": "heads_gemv_packed (vocab projection W2 of all heads, one launch)"
                           if cfg.dtype == "bf16" else "heads_gemv_f32 (vocab projection W2)",
-                "alg_bytes_per_launch": w2_bytes, "avg_launch_ms": round(w2_ms, 5)}
+                "alg_bytes_per_launch": w2_bytes, "avg_launch_ms": round(w2_ms, 5),
+                "measured_read_ceiling_GB/s": round(ceiling_gbs, 1),
+                "frac_of_measured_ceiling": round(achieved / ceiling_gbs, 4)}
 
     if args.copy_calibration:
         src = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")   # 256 MiB
@@ -282,6 +346,9 @@ def main():
         "step_alg_bytes": total_bytes,
         "step_GB/s": round(total_bytes * steps_per_s / 1e9, 1),
         "kernels": kernels,
+        "step_time_warm": warm,
+        "step_time_mall_flushed": cold,
+        "tree": {"ancestors_or_self": anc, "internal_rows": n_int},
         "greedy": t0g,
     }
     print(json.dumps(rec), flush=True)

@@ -39,10 +39,10 @@
  *   - Return value: MEDUSA_OK or a negative medusa_status.  Arguments are checked before any
  *     launch: a call that fails validation writes nothing.  A fault of earlier asynchronous work
  *     is reported as MEDUSA_ERR_HIP by the next call.  medusa_last_error() gives the text.
- *   - Workspaces: size them with the matching *_workspace() query.  A workspace must be
- *     zero-filled before its first use and not written by the caller afterwards (the kernels
- *     leave their counters at zero when they finish).  Calls that share a workspace, or that run
- *     concurrently on different streams with the same workspace, race.
+ *   - Workspaces: size them with the matching *_workspace() query.  A workspace holds only
+ *     intermediates that each call writes before it reads them, so its contents on entry do
+ *     not matter and it needs no clearing.  Two calls in flight at the same time (on different
+ *     streams) that share a workspace race.
  */
 #ifndef MEDUSA_H
 #define MEDUSA_H
@@ -121,9 +121,11 @@ size_t medusa_packed_weight_bytes(int K, long rows, int hidden);
 
 /*
  * Packs w (device, [K, rows, hidden] bf16, [out, in]) into `packed` (device,
- * medusa_packed_weight_bytes(K, rows, hidden) bytes): per head, per 16-row tile, per 32-column
- * block, the 64 lanes' 16-byte operands back to back, rows past `rows` zero-filled:
- *   packed[k][tile][kb][lane][e] = w[k][16 tile + lane % 16][32 kb + 8 (lane / 16) + e].
+ * medusa_packed_weight_bytes(K, rows, hidden) bytes).  The rows of all heads are cut into 16-row
+ * tiles; for each 32-column block kb, the 64 lanes' 16-byte operands of every tile of every head
+ * follow one another (1 KB per tile), rows past `rows` zero-filled:
+ *   packed[kb][k][tile][lane][e] = w[k][16 tile + lane % 16][32 kb + 8 (lane / 16) + e],
+ * kb < hidden / 32, tile < ceil(rows / 16), lane < 64, e < 8.
  * Done once per model, outside the decode loop.  Limits as medusa_heads.
  */
 int medusa_pack_weights(const void* w, int K, long rows, int hidden, void* packed, void* stream);
@@ -269,6 +271,16 @@ typedef enum {
  * Returns MEDUSA_ERR_ARG for an unknown kernel id or a single NULL event.
  */
 int medusa_set_kernel_events(int which, void* before, void* after);
+
+/*
+ * Streaming-read ceiling (measurement only): reads `bytes` bytes at `buf` (device, 16-byte
+ * aligned, bytes a positive multiple of 16) once, with 16-byte nontemporal loads in a grid-stride
+ * sweep, and writes nothing except possibly sink[0] (device uint32, content unspecified).  Its
+ * duration over a buffer much larger than the caches gives the read bandwidth that one plain
+ * kernel reaches, the measured ceiling beside the published HBM peak.
+ * Returns MEDUSA_ERR_ARG (null or misaligned pointer) or MEDUSA_ERR_SHAPE (bad size).
+ */
+int medusa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     pack_weights,
     medusa_heads_workspace,
     set_kernel_events,
+    stream_read,
     tree_attention,
     tree_attention_workspace,
     typical_accept,

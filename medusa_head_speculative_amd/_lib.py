@@ -37,7 +37,8 @@ class medusa_tree(ctypes.Structure):
 EXPORTS = ["medusa_last_error", "medusa_heads_workspace", "medusa_heads", "medusa_tree_dims",
            "build_tree", "tree_attention_workspace", "tree_attention",
            "typical_accept_workspace", "typical_accept", "medusa_set_kernel_events",
-           "medusa_heads_packed", "medusa_packed_weight_bytes", "medusa_pack_weights"]
+           "medusa_heads_packed", "medusa_packed_weight_bytes", "medusa_pack_weights",
+           "medusa_stream_read"]
 
 KERNELS = ["heads_w1", "heads_w2", "topk", "tree_gather", "attention", "attn_combine", "accept",
            "next_token"]
@@ -82,6 +83,8 @@ def load():
     L.medusa_pack_weights.restype = i
     L.medusa_pack_weights.argtypes = [vp, i, l, i, vp, vp]
     L.medusa_set_kernel_events.argtypes = [i, vp, vp]
+    L.medusa_stream_read.restype = i
+    L.medusa_stream_read.argtypes = [vp, sz, vp, vp]
     _lib = L
     return L
 
@@ -115,7 +118,7 @@ def dtype_code(t):
 
 
 def workspace(nbytes, device=None):
-    """A zero-filled workspace (the kernels keep their counters at zero between calls)."""
+    """A workspace of at least `nbytes` bytes (zero-filled; the kernels need no particular contents)."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
 
 
@@ -248,3 +251,11 @@ def set_kernel_events(kernel, before=None, after=None):
     b = ctypes.c_void_p(before.cuda_event) if before is not None else None
     a = ctypes.c_void_p(after.cuda_event) if after is not None else None
     _check(load().medusa_set_kernel_events(which, b, a))
+
+
+def stream_read(buf, sink, stream=None):
+    """Measurement: one streaming read of the whole of `buf` (a contiguous device tensor whose
+    size in bytes is a multiple of 16) by the library's plain read kernel; `sink` is a device
+    int32 tensor of at least one element that the kernel may write."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(load().medusa_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))

@@ -356,4 +356,14 @@ int medusa_set_kernel_events(int which, void* before, void* after) {
   return MEDUSA_OK;
 }
 
+int medusa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(MEDUSA_ERR_ARG, "null pointer");
+  if (bytes == 0 || bytes % 16 != 0) return fail(MEDUSA_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return fail(MEDUSA_ERR_ARG, "buf must be 16-byte aligned");
+  if (int st = check_pending()) return st;
+  return launched(medusa::launch_stream_read(buf, static_cast<long>(bytes / 16), sink,
+                                             static_cast<hipStream_t>(stream)),
+                  "medusa_stream_read");
+}
+
 }  // extern "C"

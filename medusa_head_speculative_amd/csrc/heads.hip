@@ -155,113 +155,142 @@ __global__ __launch_bounds__(256) void heads_gemv_bf16(const uint16_t* __restric
 // ------------------------------------------------------------------------------------------
 // bf16 weights pre-packed in MFMA fragment order
 // ------------------------------------------------------------------------------------------
-// Packed layout (medusa_pack_weights): per head, per 16-row tile, per 32-column block, the 64
-// lanes' 16-byte A fragments back to back:
-//   P[k][tile][kb][lane][e] = W[k][16*tile + lane%16][32*kb + 8*(lane/16) + e]  (0 past the rows)
-// so one wave-wide 16-byte load reads 1 KB of contiguous memory and the weights of a tile are one
-// contiguous stream: the pattern the HBM streams fastest.
-// KSPLIT = 4: the 4 waves of a work-group split the contraction for the same TPW tiles (for short
-// matrices, to keep enough bytes in flight) and meet in LDS; KSPLIT = 1: every wave owns TPW
-// tiles and the whole contraction.
-template <int TPW, int U, int KSPLIT>
+// Packed layout (medusa_pack_weights).  The rows of all K heads are cut into 16-row tiles,
+// numbered gt = k*ntiles + tile (G = K*ntiles tiles in all).  For each 32-column block kb, the
+// 64 lanes' 16-byte A fragments of tile gt sit back to back in 1 KB block number kb*G + gt:
+//   P[kb][k][tile][lane][e] = W[k][16*tile + lane%16][32*kb + 8*(lane/16) + e]   (0 past the rows)
+// One wave-wide 16-byte load reads 1 KB of contiguous memory, and waves working on neighbouring
+// tiles at the same contraction step read neighbouring kilobytes, so the resident waves sweep
+// one contiguous window of the weights together.
+// Work item = TPW consecutive tiles of one head.  KSPLIT = 4: the 4 waves of a work-group split
+// the contraction of one item and meet in LDS (short matrices: more bytes in flight).
+// KSPLIT = 1: a wave owns an item and its whole contraction; with PERSIST the grid holds about
+// two work-groups per CU and each wave takes items in grid-stride order, which keeps the window
+// that the resident waves read narrow.
+template <int TPW, int U, int KSPLIT, bool PERSIST>
 __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restrict__ Wp,
                                                           const uint16_t* __restrict__ xsrc,
                                                           int ncols, HeadsEpi ep) {
+  static_assert(KSPLIT == 1 || !PERSIST, "persistent variants own whole items");
   __shared__ float red[KSPLIT == 4 ? 4 : 1][TPW][64][4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int k = blockIdx.y;
   const long ntiles = (ep.rows + 15) >> 4;
-  const long t0 = (KSPLIT == 4 ? static_cast<long>(blockIdx.x) : static_cast<long>(blockIdx.x) * 4 + wave) * TPW;
-  if (KSPLIT == 1 && t0 >= ntiles) return;
+  const long G = ntiles * ep.K;
+  const long per_head = (ntiles + TPW - 1) / TPW;      // work items per head
   const int hd = ep.hd;
   const int nkb = hd >> 5;
+  const long kbstride = G * 512;                        // elements from block kb to kb + 1
   const int kb0 = KSPLIT == 4 ? (wave * nkb) >> 2 : 0;
   const int kb1 = KSPLIT == 4 ? ((wave + 1) * nkb) >> 2 : nkb;
   const int g = lane >> 4, n = lane & 15;
-
-  const uint16_t* ap[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    long tt = t0 + t;
-    if (tt > ntiles - 1) tt = ntiles - 1;             // ragged: valid address, result dropped
-    ap[t] = Wp + (static_cast<long>(k) * ntiles + tt) * nkb * 512 + lane * 8;
-  }
-  const uint16_t* xp = n < ncols ? xsrc + (static_cast<long>(k) * ncols * ep.mode + n) * hd + g * 8
-                                 : nullptr;
-
-  f32x4_t acc[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  int kb = kb0;
-  for (; kb + U <= kb1; kb += U) {
-    bf16x8_t a[U][TPW], x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) a[u][t] = load_bf16x8_nt(ap[t] + static_cast<long>(kb + u) * 512);
-      x[u] = x_operand(xp, kb + u);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) acc[t] = mfma16x16x32(a[u][t], x[u], acc[t]);
-  }
-  for (; kb < kb1; ++kb) {
-    bf16x8_t a[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) a[t] = load_bf16x8_nt(ap[t] + static_cast<long>(kb) * 512);
-    const bf16x8_t x = x_operand(xp, kb);
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) acc[t] = mfma16x16x32(a[t], x, acc[t]);
-  }
-
   const int B = ep.B;
-  const int lo_off = ncols > B ? B : 0;
-  if (KSPLIT == 4) {
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) red[wave][t][lane][j] = acc[t][j];
-    __syncthreads();
-    for (int o = threadIdx.x; o < 16 * TPW * B; o += 256) {
-      const int rr = o / B, b = o - rr * B;
-      const int t = rr >> 4, m = rr & 15;
-      const int lh = (m >> 2) * 16 + b, j = m & 3;
-      float y = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) y += lo_off ? red[w][t][lh][j] + red[w][t][lh + lo_off][j] : red[w][t][lh][j];
-      const long row = t0 * 16 + rr;
-      if (row < ep.rows) heads_epilogue(ep, k, row, b, y);
-    }
+  const int lo_off = ncols > B ? B : 0;                 // the first layer's vector has no lo part
+
+  long item, step, end;
+  if (PERSIST) {
+    item = static_cast<long>(blockIdx.x) * 4 + wave;
+    step = static_cast<long>(gridDim.x) * 4;
+    end = per_head * ep.K;
   } else {
+    const long i = KSPLIT == 4 ? static_cast<long>(blockIdx.x) : static_cast<long>(blockIdx.x) * 4 + wave;
+    if (KSPLIT == 1 && i >= per_head) return;
+    item = static_cast<long>(blockIdx.y) * per_head + i;
+    step = 1;
+    end = item + 1;
+  }
+
+  for (; item < end; item += step) {
+    const int k = static_cast<int>(item / per_head);
+    const long t0 = (item - static_cast<long>(k) * per_head) * TPW;
+    const uint16_t* ap[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
+      long tt = t0 + t;
+      if (tt > ntiles - 1) tt = ntiles - 1;             // ragged: valid address, result dropped
+      ap[t] = Wp + (static_cast<long>(k) * ntiles + tt) * 512 + static_cast<long>(kb0) * kbstride + lane * 8;
+    }
+    const uint16_t* xp = n < ncols ? xsrc + (static_cast<long>(k) * ncols * ep.mode + n) * hd + g * 8
+                                   : nullptr;
+
+    f32x4_t acc[TPW];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float y = acc[t][j];
-        const float ylo = __shfl_down(y, lo_off > 0 ? lo_off : 1);
-        if (lo_off) y += ylo;
-        const long row = (t0 + t) * 16 + 4 * g + j;
-        if (n < B && row < ep.rows) heads_epilogue(ep, k, row, n, y);
+    for (int t = 0; t < TPW; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    int kb = kb0;
+    for (; kb + U <= kb1; kb += U) {
+      bf16x8_t a[U][TPW], x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) a[u][t] = load_bf16x8_nt(ap[t] + u * kbstride);
+        x[u] = x_operand(xp, kb + u);
+      }
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) ap[t] += U * kbstride;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) acc[t] = mfma16x16x32(a[u][t], x[u], acc[t]);
+    }
+    for (; kb < kb1; ++kb) {
+      bf16x8_t a[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        a[t] = load_bf16x8_nt(ap[t]);
+        ap[t] += kbstride;
+      }
+      const bf16x8_t x = x_operand(xp, kb);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) acc[t] = mfma16x16x32(a[t], x, acc[t]);
+    }
+
+    if (KSPLIT == 4) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[wave][t][lane][j] = acc[t][j];
+      __syncthreads();
+      for (int o = threadIdx.x; o < 16 * TPW * B; o += 256) {
+        const int rr = o / B, b = o - rr * B;
+        const int t = rr >> 4, m = rr & 15;
+        const int lh = (m >> 2) * 16 + b, j = m & 3;
+        float y = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) y += lo_off ? red[w][t][lh][j] + red[w][t][lh + lo_off][j] : red[w][t][lh][j];
+        const long row = t0 * 16 + rr;
+        if (row < ep.rows) heads_epilogue(ep, k, row, b, y);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float y = acc[t][j];
+          const float ylo = __shfl_down(y, lo_off > 0 ? lo_off : 1);
+          if (lo_off) y += ylo;
+          const long row = (t0 + t) * 16 + 4 * g + j;
+          if (n < B && row < ep.rows) heads_epilogue(ep, k, row, n, y);
+        }
       }
     }
   }
 }
 
-// Repack [K][rows][hd] bf16 weights into the fragment order above; one thread per 16 bytes.
+// Repack [K][rows][hd] bf16 weights into the fragment order above; one thread per 16 bytes of
+// the packed tensor (block index = i / 64).
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ W, long rows,
-                                                           int hd, long total16,
+                                                           int hd, int K, long total16,
                                                            uint16_t* __restrict__ P) {
   const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= total16) return;
-  const int nkb = hd >> 5;
   const long ntiles = (rows + 15) >> 4;
+  const long G = ntiles * K;
   const int lane = static_cast<int>(i & 63);
-  const long kb = (i >> 6) % nkb;
-  const long tile_all = (i >> 6) / nkb;              // k * ntiles + tile
-  const long k = tile_all / ntiles, tile = tile_all - k * ntiles;
+  const long blk = i >> 6;
+  const long kb = blk / G;
+  const long gt = blk - kb * G;
+  const long k = gt / ntiles, tile = gt - k * ntiles;
   const long row = tile * 16 + (lane & 15);
   uint4 v = make_uint4(0, 0, 0, 0);
   if (row < rows) v = *reinterpret_cast<const uint4*>(W + (k * rows + row) * hd + kb * 32 + 8 * (lane >> 4));
@@ -398,7 +427,6 @@ HeadsWs heads_ws_layout(int B, int hd, long V, int K, int topk) {
   w.logits = take(sizeof(float) * static_cast<size_t>(B) * K * V);
   const long C = (V + kTopkChunk - 1) / kTopkChunk;
   w.part = take(sizeof(uint64_t) * static_cast<size_t>(B) * K * C * topk);
-  w.counters = take(sizeof(unsigned) * B * K);
   w.total = off;
   w.chunks = static_cast<int>(C);
   return w;
@@ -411,21 +439,26 @@ size_t packed_weight_bytes(int K, long rows, int hd) {
 hipError_t launch_pack_weights(const void* w, int K, long rows, int hd, void* packed, hipStream_t s) {
   const long total16 = static_cast<long>(packed_weight_bytes(K, rows, hd) / 16);
   pack_weights_kernel<<<static_cast<unsigned>((total16 + 255) / 256), 256, 0, s>>>(
-      static_cast<const uint16_t*>(w), rows, hd, total16, static_cast<uint16_t*>(packed));
+      static_cast<const uint16_t*>(w), rows, hd, K, total16, static_cast<uint16_t*>(packed));
   return hipGetLastError();
 }
 
-// Packed-layout kernel variants (tiles per wave, unroll, contraction split); selectable for
-// tuning through MEDUSA_W1_VARIANT / MEDUSA_W2_VARIANT.
+// Packed-layout kernel variants (tiles per wave, unroll, contraction split, persistent grid);
+// selectable for tuning through MEDUSA_W1_VARIANT / MEDUSA_W2_VARIANT.
 struct PackedVariant {
-  int tpw, u, ksplit;
+  int tpw, u, ksplit, persist;
 };
 static const PackedVariant kPackedVariants[] = {
-    {1, 8, 4}, {2, 8, 4}, {1, 8, 1}, {2, 4, 1}, {2, 8, 1}, {4, 4, 1}, {4, 8, 1}, {1, 16, 1},
-    {1, 16, 4}, {1, 4, 4}};
+    {1, 8, 4, 0}, {2, 8, 4, 0}, {1, 8, 1, 0}, {2, 4, 1, 0}, {2, 8, 1, 0}, {4, 4, 1, 0},
+    {1, 8, 1, 1}, {1, 16, 1, 1}, {2, 8, 1, 1}, {2, 4, 1, 1}, {1, 4, 1, 1}, {1, 16, 4, 0},
+    {1, 4, 4, 0}};
+// Defaults from timing each variant on MI355X at the workload shapes (hidden 4096-8192, vocab
+// 32000-128256): B <= 2 persistent with one tile per wave, B <= 4 persistent with two tiles per
+// wave, B > 4 (16 vector columns, so the x loads cost as much as the weight loads) one grid of
+// non-persistent waves with two tiles sharing each x load.
 constexpr int kDefaultW1Variant = 0;
-constexpr int kDefaultW2VariantSmallB = 2;   // B <= 4: one tile per wave, 8 blocks in flight
-constexpr int kDefaultW2Variant = 4;         // B > 4: two tiles per wave share the x operand
+static int default_w2_variant(int B) { return B <= 2 ? 10 : (B <= 4 ? 8 : 4); }
+constexpr long kPersistWgs = 512;            // about two work-groups per CU
 
 static int variant_from_env(const char* name, int dflt) {
   const char* v = getenv(name);
@@ -438,21 +471,34 @@ static void launch_packed(int variant, const uint16_t* Wp, const uint16_t* x, in
                           const HeadsEpi& ep, hipStream_t s) {
   const PackedVariant v = kPackedVariants[variant];
   const long ntiles = (ep.rows + 15) / 16;
-  const long per_block = v.ksplit == 4 ? v.tpw : 4L * v.tpw;
-  const dim3 grid(static_cast<unsigned>((ntiles + per_block - 1) / per_block), ep.K);
-#define MEDUSA_PACKED_CASE(I, T, U_, S_) \
-  case I: heads_gemv_packed<T, U_, S_><<<grid, 256, 0, s>>>(Wp, x, ncols, ep); break;
+  const long per_head = (ntiles + v.tpw - 1) / v.tpw;
+  dim3 grid;
+  if (v.persist) {
+    // the fewest rounds of 4*kPersistWgs waves, then just enough work-groups for that many
+    // rounds, so every wave gets the same number of items (give or take one)
+    const long items = per_head * ep.K;
+    const long rounds = (items + 4 * kPersistWgs - 1) / (4 * kPersistWgs);
+    grid = dim3(static_cast<unsigned>((items + 4 * rounds - 1) / (4 * rounds)));
+  } else {
+    const long per_block = v.ksplit == 4 ? 1 : 4;
+    grid = dim3(static_cast<unsigned>((per_head + per_block - 1) / per_block), ep.K);
+  }
+#define MEDUSA_PACKED_CASE(I, T, U_, S_, P_) \
+  case I: heads_gemv_packed<T, U_, S_, P_><<<grid, 256, 0, s>>>(Wp, x, ncols, ep); break;
   switch (variant) {
-    MEDUSA_PACKED_CASE(0, 1, 8, 4)
-    MEDUSA_PACKED_CASE(1, 2, 8, 4)
-    MEDUSA_PACKED_CASE(2, 1, 8, 1)
-    MEDUSA_PACKED_CASE(3, 2, 4, 1)
-    MEDUSA_PACKED_CASE(4, 2, 8, 1)
-    MEDUSA_PACKED_CASE(5, 4, 4, 1)
-    MEDUSA_PACKED_CASE(6, 4, 8, 1)
-    MEDUSA_PACKED_CASE(7, 1, 16, 1)
-    MEDUSA_PACKED_CASE(8, 1, 16, 4)
-    default: MEDUSA_PACKED_CASE(9, 1, 4, 4)
+    MEDUSA_PACKED_CASE(0, 1, 8, 4, false)
+    MEDUSA_PACKED_CASE(1, 2, 8, 4, false)
+    MEDUSA_PACKED_CASE(2, 1, 8, 1, false)
+    MEDUSA_PACKED_CASE(3, 2, 4, 1, false)
+    MEDUSA_PACKED_CASE(4, 2, 8, 1, false)
+    MEDUSA_PACKED_CASE(5, 4, 4, 1, false)
+    MEDUSA_PACKED_CASE(6, 1, 8, 1, true)
+    MEDUSA_PACKED_CASE(7, 1, 16, 1, true)
+    MEDUSA_PACKED_CASE(8, 2, 8, 1, true)
+    MEDUSA_PACKED_CASE(9, 2, 4, 1, true)
+    MEDUSA_PACKED_CASE(10, 1, 4, 1, true)
+    MEDUSA_PACKED_CASE(11, 1, 16, 4, false)
+    default: MEDUSA_PACKED_CASE(12, 1, 4, 4, false)
   }
 #undef MEDUSA_PACKED_CASE
 }
@@ -465,7 +511,6 @@ hipError_t launch_heads(const void* h, const void* w1, const void* b1, const voi
   uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xs);
   float* lg = logits ? logits : reinterpret_cast<float*>(ws + L.logits);
   uint64_t* part = reinterpret_cast<uint64_t*>(ws + L.part);
-  unsigned* counters = reinterpret_cast<unsigned*>(ws + L.counters);
 
   HeadsEpi e1{0, K, hd, hd, B, b1, h, dtype, r, dtype == 1 ? xs : nullptr, nullptr};
   HeadsEpi e2{1, K, V, hd, B, nullptr, nullptr, dtype, nullptr, nullptr, lg};
@@ -473,7 +518,7 @@ hipError_t launch_heads(const void* h, const void* w1, const void* b1, const voi
   if (dtype == 1 && packed) {
     static const int v1 = variant_from_env("MEDUSA_W1_VARIANT", kDefaultW1Variant);
     static const int v2_env = variant_from_env("MEDUSA_W2_VARIANT", -1);
-    const int v2 = v2_env >= 0 ? v2_env : (B <= 4 ? kDefaultW2VariantSmallB : kDefaultW2Variant);
+    const int v2 = v2_env >= 0 ? v2_env : default_w2_variant(B);
     hook_before(K_HEADS_W1, s);
     launch_packed(v1, static_cast<const uint16_t*>(w1), hb, B, e1, s);
     hook_after(K_HEADS_W1, s);
@@ -500,7 +545,6 @@ hipError_t launch_heads(const void* h, const void* w1, const void* b1, const voi
                                                         static_cast<long>(K) * hd, hd, e2);
     hook_after(K_HEADS_W2, s);
   }
-  (void)counters;
   hook_before(K_TOPK, s);
   topk_chunks<<<dim3(L.chunks, B * K), kTopkThreads, 0, s>>>(lg, V, topk, L.chunks, part);
   topk_merge<<<B * K, 64, 0, s>>>(part, topk, L.chunks, topk_ids, topk_logits);

@@ -24,7 +24,7 @@ inline void hook_after(int k, hipStream_t s) {
 
 // ---- heads -------------------------------------------------------------------------------
 struct HeadsWs {
-  size_t r, xs, logits, part, counters, total;
+  size_t r, xs, logits, part, total;
   int chunks;
 };
 HeadsWs heads_ws_layout(int B, int hd, long V, int K, int topk);
@@ -46,7 +46,7 @@ struct AttnPlan {
   int M;          // query rows per (b, kv head) = G * T
   int qtiles;     // work-group query tiles per (b, kv head)
   int splits;     // KV splits per (b, kv head, q tile)
-  size_t ws_o, ws_ml, ws_cnt, total;
+  size_t ws_o, ws_ml, total;
 };
 AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_prefix_len);
 hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, int dtype,
@@ -67,5 +67,8 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, lo
                                  int dmax, float temperature, float eps, float delta,
                                  int32_t* best, int32_t* accept_len, int32_t* next_token,
                                  char* ws, hipStream_t s);
+
+// ---- measurement --------------------------------------------------------------------------
+hipError_t launch_stream_read(const void* buf, long n16, uint32_t* sink, hipStream_t s);
 
 }  // namespace medusa

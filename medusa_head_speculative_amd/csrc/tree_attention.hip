@@ -19,6 +19,7 @@
 // fill the chip, the K/V range is split and a second kernel merges the partial results in a
 // fixed order.  fp32 path (small models): one wave per output row, plain FMAs.
 #include <math.h>
+#include <stdlib.h>
 
 #include "common.h"
 #include "kernels.h"
@@ -468,6 +469,12 @@ __global__ __launch_bounds__(64) void tree_attn_f32(const float* __restrict__ q,
   if (lane + 64 < D) orow[lane + 64] = o1 / l;
 }
 
+static long wg_target_from_env() {
+  const char* v = getenv("MEDUSA_ATTN_WG_TARGET");
+  const long t = v ? atol(v) : 256;
+  return t >= 1 && t <= 4096 ? t : 256;
+}
+
 AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_prefix_len) {
   AttnPlan p{};
   p.G = Hq / Hkv;
@@ -477,10 +484,12 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
   if (dtype == 1) {
     const long units = static_cast<long>(B) * Hkv * p.qtiles;
     const int ntiles = (max_prefix_len + kKvTile - 1) / kKvTile + (T + kKvTile - 1) / kKvTile;
-    // occupancy is one work-group per CU: split the K/V range so the grid is one wave of
-    // work-groups, each with at least two tiles
-    if (units < 256) {
-      long s = 256 / units;
+    // too few units to cover the CUs: split the K/V range until the grid reaches the target
+    // (256 work-groups, one per CU, unless MEDUSA_ATTN_WG_TARGET says otherwise), keeping at
+    // least two tiles per split
+    static const long target = wg_target_from_env();
+    if (units < target) {
+      long s = target / units;
       s = s < ntiles / 2 ? s : ntiles / 2;
       s = s < kMaxSplits ? s : kMaxSplits;
       p.splits = s < 1 ? 1 : static_cast<int>(s);
@@ -491,7 +500,6 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
   const size_t rows = static_cast<size_t>(p.splits) * B * Hkv * p.qtiles * kAttnRows;
   p.ws_o = take(p.splits > 1 ? rows * D * sizeof(float) : 0);
   p.ws_ml = take(p.splits > 1 ? rows * sizeof(float2) : 0);
-  p.ws_cnt = 0;
   p.total = off;
   return p;
 }

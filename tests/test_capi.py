@@ -109,6 +109,10 @@ def test_invalid_arguments_fail_before_any_launch(m):
     assert L.typical_accept(*args, 0.7, 0.09, 0.0, *outs) == -1
     assert L.typical_accept(p, 1, 1, 8, 100, p, ctypes.byref(t), 0.7, 0.09, 0.3, *outs) == -2
     assert L.typical_accept(*args, 0.7, 0.09, 0.3, p, p, p, p, 8, None) == -5
+    assert L.medusa_stream_read(p, 24, p, None) == -2
+    assert L.medusa_stream_read(p, 0, p, None) == -2
+    assert L.medusa_stream_read(None, 32, p, None) == -1
+    assert L.medusa_stream_read(ctypes.c_void_p(24), 32, p, None) == -1
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

@@ -125,8 +125,8 @@ def _pack_reference(w):
     nt = (rows + 15) // 16
     padded = np.zeros((K, nt * 16, hd), w.dtype)
     padded[:, :rows] = w
-    # [K][tile][16 rows][hd/32 kb][4 groups][8] -> [K][tile][kb][group][row][8]
-    x = padded.reshape(K, nt, 16, hd // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5)
+    # [K][tile][16 rows][hd/32 kb][4 groups][8] -> [kb][K][tile][group][row][8]
+    x = padded.reshape(K, nt, 16, hd // 32, 4, 8).transpose(3, 0, 1, 4, 2, 5)
     return np.ascontiguousarray(x).reshape(-1)
 
 
