@@ -258,8 +258,9 @@ typedef enum {
   MEDUSA_KERNEL_TREE_GATHER = 3,   /* build_tree: tokens and position ids                  */
   MEDUSA_KERNEL_ATTENTION = 4,     /* tree_attention: main kernel                          */
   MEDUSA_KERNEL_ATTN_COMBINE = 5,  /* tree_attention: merge of K/V splits (when split)     */
-  MEDUSA_KERNEL_ACCEPT = 6,        /* typical_accept: row statistics, decisions, path scan */
-  MEDUSA_KERNEL_NEXT_TOKEN = 7,    /* unused: next_token is found inside the accept kernel */
+  MEDUSA_KERNEL_ACCEPT = 6,        /* typical_accept: its three launches (row statistics,
+                                      decisions, path scan and next token)                 */
+  MEDUSA_KERNEL_NEXT_TOKEN = 7,    /* unused: next_token is found inside the accept launches */
   MEDUSA_KERNEL_COUNT = 8
 } medusa_kernel;
 

@@ -57,7 +57,7 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
 // ---- typical acceptance ------------------------------------------------------------------
 struct AcceptWs {
   size_t part, dec, total;
-  int chunks;
+  int chunks, unroll;
 };
 AcceptWs accept_ws_layout(int B, int T, long V, int n_internal);
 hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, long V,

@@ -75,6 +75,24 @@ __device__ __forceinline__ int tile_elem(int r, int c) {   // element offset of 
   return r * D + ((c ^ slot_key<D>(r)) << 3);
 }
 
+// The operand reads below touch rows whose slot key depends on the lane only (the row bits that
+// vary from read to read are above bit 3 for D = 128, above bit 4 for D = 64), so every address
+// is one per-lane base XOR a compile-time block index: no per-read address registers.
+//   K fragment (cb, kb): row cb*16 + mm, chunk kb*4 + lg  ->  (kbase ^ (kb << 5)) + cb*16*D
+//   V fragment (db, ks, hi): row ks*32 + hi*16 + 4*lg + mm/4, chunk db*2 + (mm&3)/2, +4 if mm odd
+//                        ->  (vbase ^ (db << 4)) + (ks*32 + hi*16)*D
+template <int D>
+__device__ __forceinline__ int k_frag_base(int lg, int mm) {
+  const int key = slot_key<D>(mm);
+  return mm * D + (((lg ^ key) & 3) << 3) + ((key >> 2) << 5);
+}
+template <int D>
+__device__ __forceinline__ int v_frag_base(int lg, int mm) {
+  const int r = 4 * lg + (mm >> 2);
+  const int key = slot_key<D>(r);
+  return r * D + ((((mm & 3) >> 1) ^ key) & 1) * 8 + (mm & 1) * 4 + ((key >> 1) << 4);
+}
+
 // Async loads of one 64-row K/V tile straight into LDS (no registers).  Rows past nvalid repeat
 // the last valid row: finite data whose scores the mask removes.
 template <int D>
@@ -96,6 +114,14 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kc,
   }
 }
 
+// Async load of the mask words of one tree tile for this wave's 32 query rows straight into LDS
+// (4 bytes per lane: lane l fills half l%2 of row l/2's word).  Invalid rows read node 0's word.
+__device__ __forceinline__ void issue_mask(const uint64_t* __restrict__ mask, int W, int tt,
+                                           int row_node, uint64_t* Md, int wave, int lane) {
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(mask + static_cast<long>(row_node) * W + tt) + (lane & 1);
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(Md + wave * 32), 4, 0, 0);
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
   constexpr int NKB = D / 32;            // 32-wide contraction blocks over the head dim
@@ -106,6 +132,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
   __shared__ __align__(16) uint16_t K1[TILE];
   __shared__ __align__(16) uint16_t V1[TILE];
   __shared__ int s_active[64];
+  __shared__ __align__(16) uint64_t s_mask[2][kAttnRows];   // mask words of the tree tile in flight
 
   // ---- work item; consecutive logical items (query tiles of one K/V range) share an XCD ----
   const int per_xcd = gridDim.x >> 3;
@@ -155,12 +182,18 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
     }
   };
 
+  // node whose mask word this lane stages: row wave*32 + lane/2 of the work-group
+  const int mrow_m = qt * kAttnRows + wave * 32 + (lane >> 1);
+  const int mrow_node = mrow_m < a.M ? mrow_m / a.G : 0;
+
   int t = next_active(t_begin);
+  int buf = 0;
   if (t < t_end) {
     long row0;
     int nvalid;
     tile_rows(t, row0, nvalid);
     issue_tile<D>(a.kc, a.vc, kvbase + row0, nvalid, K0, V0, wave, lane);
+    if (t >= np) issue_mask(a.mask, a.W, t - np, mrow_node, s_mask[0], wave, lane);
   }
 
   // ---- this lane's two query rows (mb = 0, 1) ----
@@ -196,11 +229,13 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
     int nvalid;
     tile_rows(t, row0, nvalid);
     const bool full = !is_tree && nvalid == kKvTile;
-    uint64_t mw[2] = {~0ull, ~0ull};
+    // visible columns of this lane's two rows: the staged mask word (tree tiles) and the valid
+    // rows of the tile; read from LDS, so nothing here waits for the next tile's loads
+    const uint64_t vmask = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
+    uint64_t mw[2] = {vmask, vmask};
     if (is_tree) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        mw[mb] = rvalid[mb] ? a.mask[static_cast<long>(node[mb]) * a.W + (t - np)] : 0ull;
+      for (int mb = 0; mb < 2; ++mb) mw[mb] &= s_mask[buf][wave * 32 + mb * 16 + mm];
     }
     const int tn = next_active(t + 1);
     if (tn < t_end) {
@@ -208,6 +243,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
       int nnvalid;
       tile_rows(tn, nrow0, nnvalid);
       issue_tile<D>(a.kc, a.vc, kvbase + nrow0, nnvalid, Kn, Vn, wave, lane);
+      if (tn >= np) issue_mask(a.mask, a.W, tn - np, mrow_node, s_mask[buf ^ 1], wave, lane);
     }
 
     // ---- scores S^T = K Q^T ----
@@ -216,11 +252,13 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) sacc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    int kb_base = k_frag_base<D>(lg, mm);
+    asm volatile("" : "+v"(kb_base));   // keep the base opaque: addresses are rebuilt per read
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8_t kf = lds_read16(Kc + tile_elem<D>(cb * 16 + mm, kb * 4 + lg));
+        const bf16x8_t kf = lds_read16(Kc + ((kb_base ^ (kb << 5)) + cb * 16 * D));
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) sacc[mb][cb] = mfma16x16x32(kf, qf[mb][kb], sacc[mb][cb]);
       }
@@ -233,14 +271,22 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float sv[4][4];
+      if (full) {
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = cb * 16 + 4 * lg + j;
-          const bool vis = full || (c < nvalid && ((mw[mb] >> c) & 1ull));
-          sv[cb][j] = vis ? sacc[mb][cb][j] : -INFINITY;
-        }
+          for (int j = 0; j < 4; ++j) sv[cb][j] = sacc[mb][cb][j];
+      } else {
+        // bits of columns cb*16 + 4*lg + j, j = 0..3, at bit 4*cb + j
+        const uint64_t sh = mw[mb] >> (4 * lg);
+        const uint32_t bits = static_cast<uint32_t>((sh & 0xFull) | ((sh >> 12) & 0xF0ull) |
+                                                    ((sh >> 24) & 0xF00ull) | ((sh >> 36) & 0xF000ull));
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sv[cb][j] = ((bits >> (4 * cb + j)) & 1u) ? sacc[mb][cb][j] : -INFINITY;
+      }
       float mx = sv[0][0];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
@@ -278,15 +324,15 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
 
     // ---- O^T += V^T P^T; contraction index 8*lg+e <-> tile column
     //      ks*32 + (e < 4 ? 4*lg + e : 16 + 4*lg + e - 4), matching the score layout ----
+    int vb_base = v_frag_base<D>(lg, mm);
+    asm volatile("" : "+v"(vb_base));
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int crow = ks * 32 + 4 * lg + (mm >> 2);
-        const int chunk = db * 2 + ((mm & 3) >> 1);
-        const int half = (mm & 1) * 4;
-        const s16x4_t v0 = lds_read_tr(Vc + tile_elem<D>(crow, chunk) + half);
-        const s16x4_t v1 = lds_read_tr(Vc + tile_elem<D>(crow + 16, chunk) + half);
+        const uint16_t* vp = Vc + ((vb_base ^ (db << 4)) + ks * 32 * D);
+        const s16x4_t v0 = lds_read_tr(vp);
+        const s16x4_t v1 = lds_read_tr(vp + 16 * D);
         typedef __attribute__((ext_vector_type(8))) short s16x8_t;
         const s16x8_t vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         const bf16x8_t va = __builtin_bit_cast(bf16x8_t, vv);
@@ -298,6 +344,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
       }
     }
     t = tn;
+    buf ^= 1;
   };
 
   while (t < t_end) {

@@ -8,12 +8,18 @@
 // (best_candidate, accept_length).  Written out: p = softmax(l / T), H = -sum p ln p,
 // accept iff p(x) > min(eps, delta * exp(-H)).
 //
-// Only internal rows are read (a leaf's row judges no child).  One work-group per
-// (sequence, internal row, 2048-element chunk) computes in a single pass the chunk's max y,
-// S = sum 2^(y - max) and A = sum (y - max) 2^(y - max) with y = l * log2(e) / T, plus the
-// argmax; the last chunk of a row to finish merges the partials in chunk order, so
-// H = ln2 * (log2 S - A / S) and ln p(x) = ln2 * (y_x - max - log2 S), and decides the row's
-// children in the log domain; the last row of a sequence to finish scans the paths.
+// Only internal rows are read (a leaf's row judges no child).  Three launches, none of whose
+// work-groups waits for another (on this GPU a release fence per work-group serialises, so each
+// handoff is a kernel boundary):
+//   accept_chunks  one work-group per (sequence, internal row, chunk) computes in a single pass
+//                  the chunk's max y, S = sum 2^(y - max) and A = sum (y - max) 2^(y - max) with
+//                  y = l * log2(e) / T, plus the argmax (a chunk is 1-8 rounds of 8 elements per
+//                  thread, the most that still leaves about a thousand work-groups);
+//   accept_rows    one work-group per (sequence, internal row) merges the row's partials in chunk
+//                  order, so H = ln2 * (log2 S - A / S) and ln p(x) = ln2 * (y_x - max - log2 S),
+//                  and decides the row's children in the log domain;
+//   accept_paths   one work-group per sequence scans the paths for the longest accepted prefix
+//                  and finds the next token.
 #include <math.h>
 
 #include "common.h"
@@ -23,7 +29,20 @@ namespace medusa {
 
 constexpr int kAccThreads = 256;
 constexpr int kAccPerThread = 8;
-constexpr int kAccChunk = kAccThreads * kAccPerThread;  // 2048
+constexpr int kAccVec = kAccThreads * kAccPerThread;    // elements per load round of a work-group
+constexpr long kPathWideBytes = 32 << 10;   // leaf rows above this size get a 1024-thread block
+constexpr int kMaxTreeTokens = 4096;
+constexpr long kAccTargetGroups = 1024;
+
+// Load rounds per chunk: the largest of 8, 4, 2 whose chunk count still gives at least
+// kAccTargetGroups work-groups, else 1 (small problems stay spread over many CUs).
+static int accept_unroll(int B, long V, int n_int) {
+  for (int u = 8; u > 1; u >>= 1) {
+    const long C = (V + static_cast<long>(kAccVec) * u - 1) / (static_cast<long>(kAccVec) * u);
+    if (C * n_int * B >= kAccTargetGroups) return u;
+  }
+  return 1;
+}
 
 struct RowStat {   // partial softmax statistics of a set of elements (log2 units)
   float m, S, A, pad;
@@ -145,9 +164,10 @@ __device__ __forceinline__ void block_merge(RowStat& st, uint64_t& arg, bool gre
   }
 }
 
-// Kernel 1, grid (C, n_int, B): statistics and argmax of one 2048-element chunk of an internal
-// row, written to the partial arrays.  No cross-work-group synchronisation: a fence per
-// work-group serialises on this GPU, so the merge is a separate launch.
+// Kernel 1, grid (C, n_int, B): statistics and argmax of one chunk (U rounds of 2048 elements)
+// of an internal row, written to the partial arrays.  All U rounds of loads are issued before
+// any is used.
+template <int U>
 __global__ __launch_bounds__(kAccThreads) void accept_chunks(AcceptArgs a) {
   __shared__ RowStat s_stat[kAccThreads / 64];
   __shared__ uint64_t s_arg[kAccThreads / 64];
@@ -155,35 +175,42 @@ __global__ __launch_bounds__(kAccThreads) void accept_chunks(AcceptArgs a) {
   const int n = a.internal[r];
   const int esz = a.dtype == 1 ? 2 : 4;
   const char* row = static_cast<const char*>(a.logits) + (static_cast<long>(b) * a.T + n) * a.V * esz;
-  const long idx0 = static_cast<long>(c) * kAccChunk + static_cast<long>(threadIdx.x) * kAccPerThread;
-  float x[kAccPerThread];
-  bool valid[kAccPerThread];
-  load8(row, a.dtype, idx0, a.V, x, valid);
+  const long base = static_cast<long>(c) * kAccVec * U + static_cast<long>(threadIdx.x) * kAccPerThread;
+  float x[U][kAccPerThread];
+  bool valid[U][kAccPerThread];
+#pragma unroll
+  for (int u = 0; u < U; ++u) load8(row, a.dtype, base + u * kAccVec, a.V, x[u], valid[u]);
   uint64_t arg = 0;
 #pragma unroll
-  for (int e = 0; e < kAccPerThread; ++e)
-    if (valid[e]) {
-      const uint64_t k = sel_key(x[e], static_cast<uint32_t>(idx0 + e));
-      arg = k > arg ? k : arg;
-    }
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < kAccPerThread; ++e)
+      if (valid[u][e]) {
+        const uint64_t k = sel_key(x[u][e], static_cast<uint32_t>(base + u * kAccVec + e));
+        arg = k > arg ? k : arg;
+      }
   RowStat st{-INFINITY, 0.f, 0.f, 0.f};
   if (!a.greedy) {
     float m = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < kAccPerThread; ++e)
-      if (valid[e]) m = fmaxf(m, x[e] * a.y_scale);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < kAccPerThread; ++e)
+        if (valid[u][e]) m = fmaxf(m, x[u][e] * a.y_scale);
     if (m > -INFINITY) {
       float S = 0.f, A = 0.f;
 #pragma unroll
-      for (int e = 0; e < kAccPerThread; ++e) {
-        if (!valid[e]) continue;
-        const float d = x[e] * a.y_scale - m;
-        const float p = exp2f(d);
-        if (p > 0.f) {
-          S += p;
-          A += d * p;
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < kAccPerThread; ++e) {
+          if (!valid[u][e]) continue;
+          const float d = x[u][e] * a.y_scale - m;
+          const float p = exp2f(d);
+          if (p > 0.f) {
+            S += p;
+            A += d * p;
+          }
         }
-      }
       st = RowStat{m, S, A, 0.f};
     }
   }
@@ -195,9 +222,33 @@ __global__ __launch_bounds__(kAccThreads) void accept_chunks(AcceptArgs a) {
   }
 }
 
+// argmax (lowest index on ties) of one row by a block of NT threads, UR rounds of 8 elements
+// per thread in flight
+template <int NT, int UR>
+__device__ __forceinline__ uint64_t block_row_argmax(const void* row, int dtype, long V,
+                                                     uint64_t* scratch) {
+  constexpr long kStep = static_cast<long>(NT) * kAccPerThread;
+  uint64_t arg = 0;
+  for (long j0 = static_cast<long>(threadIdx.x) * kAccPerThread; j0 < V; j0 += UR * kStep) {
+    float x[UR][kAccPerThread];
+    bool valid[UR][kAccPerThread];
+#pragma unroll
+    for (int u = 0; u < UR; ++u) load8(row, dtype, j0 + u * kStep, V, x[u], valid[u]);
+#pragma unroll
+    for (int u = 0; u < UR; ++u)
+#pragma unroll
+      for (int e = 0; e < kAccPerThread; ++e)
+        if (valid[u][e]) {
+          const uint64_t k = sel_key(x[u][e], static_cast<uint32_t>(j0 + u * kStep + e));
+          arg = k > arg ? k : arg;
+        }
+  }
+  return block_max_u64<NT>(arg, scratch);
+}
+
 // Kernel 2, grid (n_int, B): merges one row's C partials in chunk order (fixed tree), then
-// decides the row's children.  The children's tokens and logits are fetched while the partials
-// load.
+// decides the row's children (at most 64).  The children's tokens and logits are fetched while
+// the partials load.
 __global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
   __shared__ RowStat s_stat[kAccThreads / 64];
   __shared__ uint64_t s_arg[kAccThreads / 64];
@@ -207,7 +258,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
   const int n = a.internal[r];
   const int esz = a.dtype == 1 ? 2 : 4;
   const char* row = static_cast<const char*>(a.logits) + (static_cast<long>(b) * a.T + n) * a.V * esz;
-  const int c0 = a.child_ptr[n], nchild = a.child_ptr[n + 1] - c0;   // at most 64 children
+  const int c0 = a.child_ptr[n], nchild = a.child_ptr[n + 1] - c0;
   int child = -1, tok = -1;
   float ltok = 0.f;
   if (threadIdx.x < nchild) {
@@ -250,37 +301,20 @@ __global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
   }
 }
 
-// argmax (lowest index on ties) of one row, whole block, 4 loads in flight per thread
-__device__ __forceinline__ uint64_t block_row_argmax(const void* row, int dtype, long V,
-                                                     uint64_t* scratch) {
-  uint64_t arg = 0;
-  for (long j0 = static_cast<long>(threadIdx.x) * kAccPerThread; j0 < V; j0 += 4L * kAccChunk) {
-    float x[4][kAccPerThread];
-    bool valid[4][kAccPerThread];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) load8(row, dtype, j0 + u * kAccChunk, V, x[u], valid[u]);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int e = 0; e < kAccPerThread; ++e)
-        if (valid[u][e]) {
-          const uint64_t k = sel_key(x[u][e], static_cast<uint32_t>(j0 + u * kAccChunk + e));
-          arg = k > arg ? k : arg;
-        }
-  }
-  return block_max_u64<kAccThreads>(arg, scratch);
-}
-
-// Kernel 2, grid (B): the longest accepted prefix over the paths, and the next token.
-__global__ __launch_bounds__(kAccThreads) void accept_paths(AcceptArgs a) {
-  __shared__ uint64_t s_scratch[kAccThreads / 64];
-  __shared__ int32_t s_dec[4096];
+// Kernel 3, grid (B): the longest accepted prefix over the paths, and the next token.  When the
+// last accepted node is a leaf, its row's argmax is read here by the whole block with 8 rounds
+// of loads in flight per thread (NT = 1024 for rows above 32 KB: 128 KB at a time; else 256).
+template <int NT>
+__global__ __launch_bounds__(NT) void accept_paths(AcceptArgs a) {
+  constexpr int kPathThreads = NT;
+  __shared__ uint64_t s_scratch[kPathThreads / 64];
+  __shared__ int32_t s_dec[kMaxTreeTokens];
   const int b = blockIdx.x;
-  s_dec[0] = 1;
-  for (int i = 1 + threadIdx.x; i < a.T; i += kAccThreads) s_dec[i] = a.dec[static_cast<long>(b) * a.T + i];
+  if (threadIdx.x == 0) s_dec[0] = 1;
+  for (int i = 1 + threadIdx.x; i < a.T; i += kPathThreads) s_dec[i] = a.dec[static_cast<long>(b) * a.T + i];
   __syncthreads();
   uint64_t bestk = 0;
-  for (int p = threadIdx.x; p < a.n_paths; p += kAccThreads) {
+  for (int p = threadIdx.x; p < a.n_paths; p += kPathThreads) {
     const int32_t* path = a.paths + static_cast<long>(p) * (a.dmax + 1);
     const int len = a.path_len[p];
     int k = 0;
@@ -288,7 +322,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_paths(AcceptArgs a) {
     const uint64_t key = (static_cast<uint64_t>(k) << 32) | (0xffffffffu - static_cast<uint32_t>(p));
     bestk = key > bestk ? key : bestk;
   }
-  bestk = block_max_u64<kAccThreads>(bestk, s_scratch);
+  bestk = block_max_u64<kPathThreads>(bestk, s_scratch);
   const int p = static_cast<int>(0xffffffffu - static_cast<uint32_t>(bestk & 0xffffffffu));
   const int k = static_cast<int>(bestk >> 32);
   const int last = a.paths[static_cast<long>(p) * (a.dmax + 1) + k];
@@ -303,7 +337,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_paths(AcceptArgs a) {
   } else {
     const int esz = a.dtype == 1 ? 2 : 4;
     const char* lrow = static_cast<const char*>(a.logits) + (static_cast<long>(b) * a.T + last) * a.V * esz;
-    const uint64_t g = block_row_argmax(lrow, a.dtype, a.V, s_scratch);
+    const uint64_t g = block_row_argmax<kPathThreads, 8>(lrow, a.dtype, a.V, s_scratch);
     if (threadIdx.x == 0) a.next_token[b] = static_cast<int32_t>(sel_key_index(g));
   }
 }
@@ -312,7 +346,9 @@ AcceptWs accept_ws_layout(int B, int T, long V, int n_internal) {
   AcceptWs w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
-  const long C = (V + kAccChunk - 1) / kAccChunk;
+  w.unroll = accept_unroll(B, V, n_internal);
+  const long chunk = static_cast<long>(kAccVec) * w.unroll;
+  const long C = (V + chunk - 1) / chunk;
   w.chunks = static_cast<int>(C);
   w.part = take((sizeof(RowStat) + sizeof(uint64_t)) * static_cast<size_t>(B) * n_internal * C);
   w.dec = take(sizeof(int32_t) * static_cast<size_t>(B) * T * 2);   // decisions + row argmax
@@ -356,10 +392,19 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, lo
   a.best = best;
   a.accept_len = accept_len;
   a.next_token = next_token;
+  const dim3 grid(L.chunks, n_internal, B);
   hook_before(K_ACCEPT, s);
-  accept_chunks<<<dim3(L.chunks, n_internal, B), kAccThreads, 0, s>>>(a);
+  switch (L.unroll) {
+    case 8: accept_chunks<8><<<grid, kAccThreads, 0, s>>>(a); break;
+    case 4: accept_chunks<4><<<grid, kAccThreads, 0, s>>>(a); break;
+    case 2: accept_chunks<2><<<grid, kAccThreads, 0, s>>>(a); break;
+    default: accept_chunks<1><<<grid, kAccThreads, 0, s>>>(a); break;
+  }
   accept_rows<<<dim3(n_internal, B), kAccThreads, 0, s>>>(a);
-  accept_paths<<<B, kAccThreads, 0, s>>>(a);
+  if (V * (dtype == 1 ? 2 : 4) > kPathWideBytes)
+    accept_paths<1024><<<B, 1024, 0, s>>>(a);
+  else
+    accept_paths<256><<<B, 256, 0, s>>>(a);
   hook_after(K_ACCEPT, s);
   return hipGetLastError();
 }

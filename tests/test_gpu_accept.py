@@ -76,6 +76,7 @@ def test_accept_full_size(ci, temp):
 @pytest.mark.parametrize("V,tree,B,temp", [
     (1, "one", 1, 0.7), (7, "c0", 2, 0.7), (2047, "c1", 3, 1.0), (2049, "c1", 3, 0.0),
     (5000, "chain6", 2, 0.7), (4100, "c3", 5, 0.3), (300, "c2", 8, 3.0),
+    (20001, "c4", 5, 0.7),      # 8 load rounds per chunk, ragged last chunk and vector tail
 ])
 def test_accept_edges(dtype, V, tree, B, temp):
     m = lib()
