@@ -184,6 +184,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
 
   // node whose mask word this lane stages: row wave*32 + lane/2 of the work-group
   const int mrow_m = qt * kAttnRows + wave * 32 + (lane >> 1);
+  // a wave whose rows are all past M only helps stage tiles and meets the barriers
+  const bool wave_active = qt * kAttnRows + wave * 32 < a.M;
   const int mrow_node = mrow_m < a.M ? mrow_m / a.G : 0;
 
   int t = next_active(t_begin);
@@ -244,6 +246,11 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
       tile_rows(tn, nrow0, nnvalid);
       issue_tile<D>(a.kc, a.vc, kvbase + nrow0, nnvalid, Kn, Vn, wave, lane);
       if (tn >= np) issue_mask(a.mask, a.W, tn - np, mrow_node, s_mask[buf ^ 1], wave, lane);
+    }
+    if (!wave_active) {
+      t = tn;
+      buf ^= 1;
+      return;
     }
 
     // ---- scores S^T = K Q^T ----

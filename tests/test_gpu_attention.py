@@ -66,6 +66,7 @@ CASES = [
     ("bf16", 2, 16, 2, 64, "c2", [127, 300]),
     ("bf16", 1, 8, 8, 128, "c4", [5]),
     ("bf16", 1, 4, 1, 128, "chain8", [700]),
+    ("bf16", 1, 16, 1, 64, "c3", [90]),           # 2064 query rows: 9 tiles of 8 waves
     ("bf16", 2, 4, 4, 128, "one", [0, 3]),
     ("f32", 2, 4, 2, 64, "c1", [0, 77]),
     ("f32", 1, 2, 2, 128, "c0", [1]),
