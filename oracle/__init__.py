@@ -4,13 +4,14 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the benchma
 baseline, never by the HIP library or its Python binding.  It shares no code with them.
 
 Parts: heads + top-k (heads.py, C loops in medusa_oracle.c), the candidate tree (tree.py),
-tree-masked attention (attention.py, C loops) and typical acceptance (accept.py).  step.py
-chains them.
+tree-masked attention (attention.py, C loops), typical acceptance (accept.py) and the commit of
+the accepted candidate into the cache (commit.py).
 """
 
 from . import _clib  # noqa: F401
 from .accept import row_threshold, typical_accept  # noqa: F401
 from .attention import tree_attention  # noqa: F401
+from .commit import commit  # noqa: F401
 from .heads import heads, project, topk, topk_ties  # noqa: F401
 from .tree import TreeError, build_static, canonical, gather  # noqa: F401
 
