@@ -208,20 +208,28 @@ def main():
 
     # ---- per-kernel breakdown: a separate pass with every kernel bracketed by events (the
     #      extra event records slow the step, so this pass is not the headline) ----
+    #      The commit of the accepted candidate (the decode-loop glue after the step) is timed
+    #      here too, on copies of the caches so that the step's inputs stay fixed. ----
     splits = step.ws_attn.numel() > 256
-    names = ["heads_w1", "heads_w2", "topk", "tree_gather", "attention", "accept"]
+    names = ["heads_w1", "heads_w2", "topk", "tree_gather", "attention", "accept", "commit"]
     if splits:
         names.insert(5, "attn_combine")
+    kc_commit, vc_commit = kc.clone(), vc.clone()
     nb = max(10, min(args.steps, 50))
     events = {k: make_events(nb) for k in names}
     for i in range(nb):
         for k in names:
             m.set_kernel_events(k, *events[k][i])
         run(temperature)
+        step.commit(kc_commit, vc_commit, pl)
     torch.cuda.synchronize()
+    del kc_commit, vc_commit
     for k in names:
         m.set_kernel_events(k, None, None)
     kb = kernel_bytes(cfg, T, n_int)
+    # commit: each accepted node's K and V rows read and written once, plus the emitted tokens
+    moved = int(step.accept_length.cpu().numpy().sum())
+    kb["commit"] = 4 * moved * cfg.Hkv * cfg.D * cfg.esize + cfg.B * (step.tree.dims["dmax"] + 1) * 4
     kernels = {}
     for k, evs in events.items():
         ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))

@@ -247,10 +247,41 @@ int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
                    size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------- *
+ * 5. Commit of the accepted candidate (decode-loop glue)
+ * ---------------------------------------------------------------------------------------- */
+
+/*
+ * After typical_accept: emits the accepted tokens, compacts their K/V in the cache and hands
+ * over what the next step starts from (Wiblog page, inference-flow section: the accepted prefix
+ * is output and the next round starts from the last accepted token; the verification logits
+ * already give that round's first token).  For each sequence b, with p = best_candidate[b],
+ * a = accept_length[b], L = prefix_len[b] and path = tree->paths[p] (node per depth):
+ *   out_tokens[b][k]  = tokens[b][path[k]] for k <= a, -1 for a < k <= dmax    [B][dmax + 1]
+ *   out_count[b]      = a + 1
+ *   k_cache, v_cache  row L + k of every kv head <- row L + path[k], k = 1 .. a, in place (the
+ *                     root already sits at row L); no other row changes
+ *   new_prefix_len[b] = L + a + 1              (may be the same array as prefix_len)
+ *   new_root[b]       = next_token[b]          (nullable: skipped)
+ *   next_hidden[b][:] = hidden[b][path[a]][:]  (hidden [B][T][hidden_size] and next_hidden
+ *                                               [B][hidden_size] in dtype; both NULL skips it)
+ * A sequence whose p, a or L is out of range (p >= n_paths, a > path_len[p], L < 0 or
+ * L + T > lcap) is left untouched and gets out_count[b] = 0, new_prefix_len[b] = L.
+ * All pointers are device memory; tokens must not overlap out_tokens.
+ * Limits: dtype F32 or BF16; D * element size and hidden_size * element size multiples of 16;
+ *         1 <= B <= 65535, 1 <= Hkv <= 256.
+ */
+int commit_accepted(const medusa_tree* tree, int B, const int32_t* best_candidate,
+                    const int32_t* accept_length, const int32_t* tokens,
+                    const int32_t* next_token, void* k_cache, void* v_cache, int dtype, int Hkv,
+                    long lcap, int D, const int32_t* prefix_len, int32_t* new_prefix_len,
+                    int32_t* out_tokens, int32_t* out_count, int32_t* new_root,
+                    const void* hidden, int hidden_size, void* next_hidden, void* stream);
+
+/* ---------------------------------------------------------------------------------------- *
  * Measurement hook (not part of the method)
  * ---------------------------------------------------------------------------------------- */
 
-/* The kernels the four entry points launch, for per-kernel timing. */
+/* The kernels the entry points launch, for per-kernel timing. */
 typedef enum {
   MEDUSA_KERNEL_HEADS_W1 = 0,      /* medusa_heads: first layer, r = h + SiLU(W1 h + b1)   */
   MEDUSA_KERNEL_HEADS_W2 = 1,      /* medusa_heads: vocab projection, logits = W2 r        */
@@ -260,7 +291,7 @@ typedef enum {
   MEDUSA_KERNEL_ATTN_COMBINE = 5,  /* tree_attention: merge of K/V splits (when split)     */
   MEDUSA_KERNEL_ACCEPT = 6,        /* typical_accept: its three launches (row statistics,
                                       decisions, path scan and next token)                 */
-  MEDUSA_KERNEL_NEXT_TOKEN = 7,    /* unused: next_token is found inside the accept launches */
+  MEDUSA_KERNEL_COMMIT = 7,        /* commit_accepted                                      */
   MEDUSA_KERNEL_COUNT = 8
 } medusa_kernel;
 

@@ -1,7 +1,7 @@
 """MI355X-native Medusa verification step: Python binding of libmedusa_hip.so.
 
 Entry points (same names as the C ABI in include/medusa.h): medusa_heads, build_tree,
-tree_attention, typical_accept, their *_workspace queries, the Tree helper (device arrays of a
+tree_attention, typical_accept, commit_accepted, their *_workspace queries, the Tree helper (device arrays of a
 fixed tree) and VerifyStep (the four calls chained on one stream).
 """
 
@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     MedusaError,
     Tree,
     build_tree,
+    commit_accepted,
     load,
     medusa_heads,
     medusa_heads_packed,

@@ -38,10 +38,10 @@ EXPORTS = ["medusa_last_error", "medusa_heads_workspace", "medusa_heads", "medus
            "build_tree", "tree_attention_workspace", "tree_attention",
            "typical_accept_workspace", "typical_accept", "medusa_set_kernel_events",
            "medusa_heads_packed", "medusa_packed_weight_bytes", "medusa_pack_weights",
-           "medusa_stream_read"]
+           "medusa_stream_read", "commit_accepted"]
 
 KERNELS = ["heads_w1", "heads_w2", "topk", "tree_gather", "attention", "attn_combine", "accept",
-           "next_token"]
+           "commit"]
 
 _lib = None
 
@@ -85,6 +85,9 @@ def load():
     L.medusa_set_kernel_events.argtypes = [i, vp, vp]
     L.medusa_stream_read.restype = i
     L.medusa_stream_read.argtypes = [vp, sz, vp, vp]
+    L.commit_accepted.restype = i
+    L.commit_accepted.argtypes = [ctypes.POINTER(medusa_tree), i, vp, vp, vp, vp, vp, vp, i, i, l,
+                                  i, vp, vp, vp, vp, vp, vp, i, vp, vp]
     _lib = L
     return L
 
@@ -240,6 +243,22 @@ def typical_accept(logits, tokens, tree, temperature, posterior_threshold, poste
                                  ctypes.byref(tree.c), temperature, posterior_threshold,
                                  posterior_alpha, _ptr(best_candidate), _ptr(accept_length),
                                  _ptr(next_token), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def commit_accepted(tree, best_candidate, accept_length, tokens, next_token, k_cache, v_cache,
+                    prefix_len, new_prefix_len, out_tokens, out_count, new_root=None, hidden=None,
+                    next_hidden=None, stream=None):
+    """Emit the accepted tokens, compact their K/V rows in the cache (in place), advance the
+    prefix and hand over the next root and hidden state (see include/medusa.h).  Caches
+    [B, Hkv, lcap, D]; out_tokens [B, dmax + 1]; hidden [B, T, Hd] / next_hidden [B, Hd]."""
+    B, Hkv, lcap, D = k_cache.shape
+    hd = 0 if hidden is None else hidden.shape[2]
+    _check(load().commit_accepted(ctypes.byref(tree.c), B, _ptr(best_candidate),
+                                  _ptr(accept_length), _ptr(tokens), _ptr(next_token),
+                                  _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), Hkv, lcap, D,
+                                  _ptr(prefix_len), _ptr(new_prefix_len), _ptr(out_tokens),
+                                  _ptr(out_count), _ptr(new_root), _ptr(hidden), hd,
+                                  _ptr(next_hidden), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------------------------

@@ -346,6 +346,58 @@ int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
                   "typical_accept");
 }
 
+// ---- commit of the accepted candidate --------------------------------------------------------
+int commit_accepted(const medusa_tree* tree, int B, const int32_t* best_candidate,
+                    const int32_t* accept_length, const int32_t* tokens,
+                    const int32_t* next_token, void* k_cache, void* v_cache, int dtype, int Hkv,
+                    long lcap, int D, const int32_t* prefix_len, int32_t* new_prefix_len,
+                    int32_t* out_tokens, int32_t* out_count, int32_t* new_root,
+                    const void* hidden, int hidden_size, void* next_hidden, void* stream) {
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_DTYPE, "dtype = %d", dtype);
+  if (!tree || !best_candidate || !accept_length || !tokens || !k_cache || !v_cache ||
+      !prefix_len || !new_prefix_len || !out_tokens || !out_count)
+    return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
+  if (new_root && !next_token) return fail(MEDUSA_ERR_ARG, "new_root needs next_token");
+  if ((hidden == nullptr) != (next_hidden == nullptr))
+    return fail(MEDUSA_ERR_ARG, "give both hidden and next_hidden or neither");
+  if (!tree->paths || !tree->path_len) return fail(MEDUSA_ERR_ARG, "a tree array is NULL");
+  if (tree->T < 1 || tree->T > 4096 || tree->n_paths < 1 || tree->dmax < 0 || tree->dmax >= tree->T)
+    return fail(MEDUSA_ERR_TREE, "tree dims are inconsistent");
+  if (B < 1 || B > 65535) return fail(MEDUSA_ERR_SHAPE, "B = %d", B);
+  if (Hkv < 1 || Hkv > 256) return fail(MEDUSA_ERR_SHAPE, "Hkv = %d", Hkv);
+  const int esz = dtype == MEDUSA_BF16 ? 2 : 4;
+  if (D < 1 || (D * esz) % 16 != 0) return fail(MEDUSA_ERR_SHAPE, "D = %d: D * element size must be a multiple of 16", D);
+  if (lcap < tree->T) return fail(MEDUSA_ERR_SHAPE, "lcap = %ld < T = %d", lcap, tree->T);
+  if (hidden && (hidden_size < 1 || (static_cast<long>(hidden_size) * esz) % 16 != 0))
+    return fail(MEDUSA_ERR_SHAPE, "hidden_size = %d: hidden_size * element size must be a multiple of 16", hidden_size);
+  int rc;
+  if ((rc = check_pending())) return rc;
+  medusa::CommitArgs a{};
+  a.paths = tree->paths;
+  a.path_len = tree->path_len;
+  a.n_paths = tree->n_paths;
+  a.dmax = tree->dmax;
+  a.T = tree->T;
+  a.best = best_candidate;
+  a.accept_len = accept_length;
+  a.tokens = tokens;
+  a.next_token = next_token;
+  a.kc = static_cast<char*>(k_cache);
+  a.vc = static_cast<char*>(v_cache);
+  a.Hkv = Hkv;
+  a.lcap = lcap;
+  a.row_bytes = D * esz;
+  a.prefix_len = prefix_len;
+  a.new_prefix_len = new_prefix_len;
+  a.out_tokens = out_tokens;
+  a.out_count = out_count;
+  a.new_root = new_root;
+  a.hidden = static_cast<const char*>(hidden);
+  a.hidden_bytes = hidden ? hidden_size * esz : 0;
+  a.next_hidden = static_cast<char*>(next_hidden);
+  return launched(medusa::launch_commit(a, B, static_cast<hipStream_t>(stream)), "commit_accepted");
+}
+
 // ---- measurement hook ------------------------------------------------------------------------
 int medusa_set_kernel_events(int which, void* before, void* after) {
   if (which < 0 || which >= medusa::kKernelCount) return fail(MEDUSA_ERR_ARG, "kernel id %d", which);

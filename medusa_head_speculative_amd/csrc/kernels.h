@@ -10,7 +10,7 @@ namespace medusa {
 // ---- per-kernel timing hook (medusa_set_kernel_events) -----------------------------------
 constexpr int kKernelCount = 8;
 enum KernelId { K_HEADS_W1 = 0, K_HEADS_W2, K_TOPK, K_TREE_GATHER, K_ATTENTION, K_ATTN_COMBINE,
-                K_ACCEPT, K_NEXT_TOKEN };
+                K_ACCEPT, K_COMMIT };
 struct EventHook {
   hipEvent_t before = nullptr, after = nullptr;
 };
@@ -67,6 +67,31 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, lo
                                  int dmax, float temperature, float eps, float delta,
                                  int32_t* best, int32_t* accept_len, int32_t* next_token,
                                  char* ws, hipStream_t s);
+
+// ---- commit of the accepted candidate ----------------------------------------------------------
+struct CommitArgs {
+  const int32_t* paths;        // [n_paths][dmax + 1]
+  const int32_t* path_len;     // [n_paths]
+  int n_paths, dmax, T;
+  const int32_t* best;
+  const int32_t* accept_len;
+  const int32_t* tokens;       // [B][T]
+  const int32_t* next_token;   // [B]
+  char* kc;                    // [B][Hkv][lcap][D]
+  char* vc;
+  int Hkv;
+  long lcap;
+  int row_bytes;               // D * element size, a multiple of 16
+  const int32_t* prefix_len;
+  int32_t* new_prefix_len;
+  int32_t* out_tokens;         // [B][dmax + 1]
+  int32_t* out_count;
+  int32_t* new_root;           // nullable
+  const char* hidden;          // [B][T][hd], nullable
+  int hidden_bytes;            // hd * element size, a multiple of 16
+  char* next_hidden;           // [B][hd], nullable
+};
+hipError_t launch_commit(const CommitArgs& a, int B, hipStream_t s);
 
 // ---- measurement --------------------------------------------------------------------------
 hipError_t launch_stream_read(const void* buf, long n16, uint32_t* sink, hipStream_t s);

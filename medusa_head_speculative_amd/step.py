@@ -1,4 +1,5 @@
-"""One verification step on one stream: heads -> tree -> tree attention -> typical acceptance.
+"""One verification step on one stream: heads -> tree -> tree attention -> typical acceptance,
+then (commit) the accepted candidate into the cache for the next step.
 
 Holds the device buffers and workspaces of a fixed shape so the timed loop allocates nothing.
 Inputs the step does not produce (the last hidden state, the tree tokens' Q/K/V inside the cache,
@@ -26,6 +27,10 @@ class VerifyStep:
         self.best = torch.zeros(B, **i32)
         self.accept_length = torch.zeros(B, **i32)
         self.next_token = torch.zeros(B, **i32)
+        self.out_tokens = torch.zeros((B, self.tree.dims["dmax"] + 1), **i32)
+        self.out_count = torch.zeros(B, **i32)
+        self.new_prefix_len = torch.zeros(B, **i32)
+        self.new_root = torch.zeros(B, **i32)
         self.ws_heads = _lib.workspace(_lib.medusa_heads_workspace(B, hidden, vocab, K, topk), device)
         self.ws_attn = _lib.workspace(_lib.tree_attention_workspace(B, Hq, Hkv, T, D, max_prefix_len), device)
         self.ws_acc = _lib.workspace(
@@ -60,3 +65,11 @@ class VerifyStep:
         self.build(root_tokens, prefix_len, stream)
         self.attention(q, k_cache, v_cache, prefix_len, attn_out, stream)
         self.accept(verif_logits, temperature, eps, delta, stream=stream)
+
+    def commit(self, k_cache, v_cache, prefix_len, hidden=None, next_hidden=None, stream=None):
+        """After accept: emit the accepted tokens (out_tokens, out_count), move their K/V rows
+        into place, and set new_prefix_len / new_root (and next_hidden from hidden)."""
+        _lib.commit_accepted(self.tree, self.best, self.accept_length, self.tokens,
+                             self.next_token, k_cache, v_cache, prefix_len, self.new_prefix_len,
+                             self.out_tokens, self.out_count, new_root=self.new_root,
+                             hidden=hidden, next_hidden=next_hidden, stream=stream)

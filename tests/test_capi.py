@@ -109,6 +109,14 @@ def test_invalid_arguments_fail_before_any_launch(m):
     assert L.typical_accept(*args, 0.7, 0.09, 0.0, *outs) == -1
     assert L.typical_accept(p, 1, 1, 8, 100, p, ctypes.byref(t), 0.7, 0.09, 0.3, *outs) == -2
     assert L.typical_accept(*args, 0.7, 0.09, 0.3, p, p, p, p, 8, None) == -5
+    ca = [ctypes.byref(t), 2, p, p, p, p, p, p]                 # tree .. v_cache
+    rest = [p, p, p, p, p, None, 0, None, None]                   # prefix .. stream
+    assert L.commit_accepted(*ca, 7, 4, 64, 128, *rest) == -3
+    assert L.commit_accepted(None, *ca[1:], 1, 4, 64, 128, *rest) == -1
+    assert L.commit_accepted(ctypes.byref(t), 0, *ca[2:], 1, 4, 64, 128, *rest) == -2
+    assert L.commit_accepted(*ca, 1, 4, 64, 4, *rest) == -2        # 4 bf16 = 8 bytes per row
+    assert L.commit_accepted(*ca, 1, 4, 5, 128, *rest) == -2       # lcap < T
+    assert L.commit_accepted(*ca, 1, 4, 64, 128, p, p, p, p, p, p, 64, None, None) == -1
     assert L.medusa_stream_read(p, 24, p, None) == -2
     assert L.medusa_stream_read(p, 0, p, None) == -2
     assert L.medusa_stream_read(None, 32, p, None) == -1

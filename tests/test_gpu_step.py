@@ -51,4 +51,19 @@ def test_step_end_to_end(ci):
         for b in range(cfg.B):
             assert (int(got[0][b]), int(got[1][b]), int(got[2][b])) in cands[b]
         print(f"{cfg.name} T={temp}: best {got[0].tolist()} accept_length {got[1].tolist()}")
+        # ---- commit the accepted candidate (on copies of the caches) against the oracle ----
+        kc2, vc2 = kc.clone(), vc.clone()
+        hid = np.arange(cfg.B * st["T"] * 16, dtype=np.float32).reshape(cfg.B, st["T"], 16)
+        hid = hid.view(np.uint32).astype(np.uint16) if cfg.dtype == "bf16" else hid
+        nh = torch.zeros((cfg.B, 16), dtype=torch.bfloat16 if cfg.dtype == "bf16" else torch.float32,
+                         device="cuda")
+        step.commit(kc2, vc2, dev(pl), hidden=dev(hid), next_hidden=nh)
+        torch.cuda.synchronize()
+        ref = oracle.commit(st, got[0], got[1], tokens, got[2], a["k_cache"], a["v_cache"], pl, hid)
+        assert np.array_equal(host(kc2), ref["k_cache"]) and np.array_equal(host(vc2), ref["v_cache"])
+        assert np.array_equal(host(step.out_tokens), ref["out_tokens"])
+        assert np.array_equal(host(step.out_count), ref["out_count"])
+        assert np.array_equal(host(step.new_prefix_len), ref["prefix_len"])
+        assert np.array_equal(host(step.new_root), ref["new_root"])
+        assert np.array_equal(host(nh), ref["next_hidden"])
 
