@@ -218,6 +218,27 @@ int tree_attention(const void* q, const void* k_cache, const void* v_cache, int 
                    const uint64_t* mask, int B, int Hq, int Hkv, int T, int D, float scale,
                    void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * tree_attention with the rotary position embedding applied first (Wiblog page, tree-attention
+ * section: the position encoding follows the tree so that each token gets its correct position
+ * index; the pages do not name the encoding, this is the rotary one of LLaMA-family models).
+ * position_ids [B][T] int32 (device; build_tree's, prefix_len + depth).  For every query row
+ * (b, hq, i) and every tree key row prefix_len[b] + i of k_cache (all kv heads), dimension
+ * j < D/2 and its partner j + D/2 turn by the angle position_ids[b][i] * rope_base^(-2j/D):
+ *     (x_j, x_{j+D/2}) -> (x_j cos - x_{j+D/2} sin,  x_j sin + x_{j+D/2} cos),
+ * in fp32 with the angle reduced in fp64, rounded to dtype (nearest even).  The rotated keys
+ * are written back into k_cache (call once per step: the prefix rows are taken as already
+ * rotated); q is left unchanged (its rotated copy lives in the workspace).  Then exactly
+ * tree_attention on the rotated queries and keys.  Arguments, limits and errors as
+ * tree_attention, plus rope_base > 1 (10000 for LLaMA-family models).
+ */
+size_t tree_attention_rope_workspace(int B, int Hq, int Hkv, int T, int D, int max_prefix_len);
+int tree_attention_rope(const void* q, void* k_cache, const void* v_cache, int dtype,
+                        const int32_t* prefix_len, int max_prefix_len, long lcap,
+                        const uint64_t* mask, const int32_t* position_ids, float rope_base,
+                        int B, int Hq, int Hkv, int T, int D, float scale, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------------------- *
  * 4. Typical acceptance
  * ---------------------------------------------------------------------------------------- */
@@ -292,7 +313,8 @@ typedef enum {
   MEDUSA_KERNEL_ACCEPT = 6,        /* typical_accept: its three launches (row statistics,
                                       decisions, path scan and next token)                 */
   MEDUSA_KERNEL_COMMIT = 7,        /* commit_accepted                                      */
-  MEDUSA_KERNEL_COUNT = 8
+  MEDUSA_KERNEL_ROPE = 8,          /* tree_attention_rope: the rotation before attention   */
+  MEDUSA_KERNEL_COUNT = 9
 } medusa_kernel;
 
 /*

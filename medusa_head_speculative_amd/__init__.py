@@ -22,6 +22,8 @@ from ._lib import (  # noqa: F401
     set_kernel_events,
     stream_read,
     tree_attention,
+    tree_attention_rope,
+    tree_attention_rope_workspace,
     tree_attention_workspace,
     typical_accept,
     typical_accept_workspace,

@@ -38,10 +38,11 @@ EXPORTS = ["medusa_last_error", "medusa_heads_workspace", "medusa_heads", "medus
            "build_tree", "tree_attention_workspace", "tree_attention",
            "typical_accept_workspace", "typical_accept", "medusa_set_kernel_events",
            "medusa_heads_packed", "medusa_packed_weight_bytes", "medusa_pack_weights",
-           "medusa_stream_read", "commit_accepted"]
+           "medusa_stream_read", "commit_accepted", "tree_attention_rope_workspace",
+           "tree_attention_rope"]
 
 KERNELS = ["heads_w1", "heads_w2", "topk", "tree_gather", "attention", "attn_combine", "accept",
-           "commit"]
+           "commit", "rope"]
 
 _lib = None
 
@@ -85,6 +86,11 @@ def load():
     L.medusa_set_kernel_events.argtypes = [i, vp, vp]
     L.medusa_stream_read.restype = i
     L.medusa_stream_read.argtypes = [vp, sz, vp, vp]
+    L.tree_attention_rope_workspace.restype = sz
+    L.tree_attention_rope_workspace.argtypes = [i, i, i, i, i, i]
+    L.tree_attention_rope.restype = i
+    L.tree_attention_rope.argtypes = [vp, vp, vp, i, vp, i, l, vp, vp, f, i, i, i, i, i, f, vp,
+                                      vp, sz, vp]
     L.commit_accepted.restype = i
     L.commit_accepted.argtypes = [ctypes.POINTER(medusa_tree), i, vp, vp, vp, vp, vp, vp, i, i, l,
                                   i, vp, vp, vp, vp, vp, vp, i, vp, vp]
@@ -228,6 +234,22 @@ def tree_attention(q, k_cache, v_cache, prefix_len, max_prefix_len, mask, out, w
     _check(load().tree_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), dtype_code(q),
                                  _ptr(prefix_len), max_prefix_len, lcap, _ptr(mask), B, Hq, Hkv, T,
                                  D, scale, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tree_attention_rope_workspace(B, Hq, Hkv, T, D, max_prefix_len):
+    return load().tree_attention_rope_workspace(B, Hq, Hkv, T, D, max_prefix_len)
+
+
+def tree_attention_rope(q, k_cache, v_cache, prefix_len, max_prefix_len, mask, position_ids,
+                        out, ws, rope_base=10000.0, scale=0.0, stream=None):
+    """tree_attention after rotating the tree tokens' q (into ws) and their k_cache rows (in
+    place) at position_ids [B,T]."""
+    B, Hq, T, D = q.shape
+    Hkv, lcap = k_cache.shape[1], k_cache.shape[2]
+    _check(load().tree_attention_rope(_ptr(q), _ptr(k_cache), _ptr(v_cache), dtype_code(q),
+                                      _ptr(prefix_len), max_prefix_len, lcap, _ptr(mask),
+                                      _ptr(position_ids), rope_base, B, Hq, Hkv, T, D, scale,
+                                      _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------------------------

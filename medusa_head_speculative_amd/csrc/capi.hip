@@ -305,6 +305,58 @@ int tree_attention(const void* q, const void* k_cache, const void* v_cache, int 
                   "tree_attention");
 }
 
+// ---- tree attention with rotary embedding at depth positions ---------------------------------
+static size_t rope_q_bytes(int B, int Hq, int T, int D) {
+  return (static_cast<size_t>(B) * Hq * T * D * sizeof(float) + 255) & ~size_t(255);
+}
+
+size_t tree_attention_rope_workspace(int B, int Hq, int Hkv, int T, int D, int max_prefix_len) {
+  if (attn_shape(B, Hq, Hkv, T, D, max_prefix_len) != MEDUSA_OK) return 0;
+  return rope_q_bytes(B, Hq, T, D) + medusa::attn_plan(1, B, Hq, Hkv, T, D, max_prefix_len).total;
+}
+
+int tree_attention_rope(const void* q, void* k_cache, const void* v_cache, int dtype,
+                        const int32_t* prefix_len, int max_prefix_len, long lcap,
+                        const uint64_t* mask, const int32_t* position_ids, float rope_base,
+                        int B, int Hq, int Hkv, int T, int D, float scale, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_DTYPE, "dtype = %d", dtype);
+  if (!q || !k_cache || !v_cache || !prefix_len || !mask || !position_ids || !out)
+    return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
+  int rc = attn_shape(B, Hq, Hkv, T, D, max_prefix_len);
+  if (rc) return rc;
+  if (lcap < static_cast<long>(max_prefix_len) + T) return fail(MEDUSA_ERR_SHAPE, "lcap = %ld < max_prefix_len + T", lcap);
+  if (!(rope_base > 1.f) || !std::isfinite(rope_base)) return fail(MEDUSA_ERR_ARG, "rope_base = %g, need > 1", rope_base);
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(static_cast<float>(D));
+  if (!std::isfinite(scale)) return fail(MEDUSA_ERR_ARG, "scale is not finite");
+  const size_t qb = rope_q_bytes(B, Hq, T, D);
+  const size_t need = qb + medusa::attn_plan(dtype, B, Hq, Hkv, T, D, max_prefix_len).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if ((rc = check_pending())) return rc;
+  char* ws = static_cast<char*>(workspace);
+  medusa::RopeArgs r{};
+  r.q = q;
+  r.q_rot = ws;
+  r.kc = k_cache;
+  r.prefix_len = prefix_len;
+  r.pos = position_ids;
+  r.base = rope_base;
+  r.B = B;
+  r.Hq = Hq;
+  r.Hkv = Hkv;
+  r.T = T;
+  r.D = D;
+  r.Lmax = max_prefix_len;
+  r.lcap = lcap;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = launched(medusa::launch_rope_tree(r, dtype, st), "tree_attention_rope"))) return rc;
+  return launched(medusa::launch_tree_attention(ws, k_cache, v_cache, dtype, prefix_len,
+                                                max_prefix_len, lcap, mask, B, Hq, Hkv, T, D,
+                                                scale, out, ws + qb, st),
+                  "tree_attention_rope");
+}
+
 // ---- typical acceptance ---------------------------------------------------------------------
 size_t typical_accept_workspace(int B, int T, long vocab, int n_internal) {
   if (B < 1 || T < 2 || T > 4096 || vocab < 1 || vocab >= (1l << 31) || n_internal < 1 || n_internal >= T) return 0;

@@ -8,9 +8,9 @@
 namespace medusa {
 
 // ---- per-kernel timing hook (medusa_set_kernel_events) -----------------------------------
-constexpr int kKernelCount = 8;
+constexpr int kKernelCount = 9;
 enum KernelId { K_HEADS_W1 = 0, K_HEADS_W2, K_TOPK, K_TREE_GATHER, K_ATTENTION, K_ATTN_COMBINE,
-                K_ACCEPT, K_COMMIT };
+                K_ACCEPT, K_COMMIT, K_ROPE };
 struct EventHook {
   hipEvent_t before = nullptr, after = nullptr;
 };
@@ -92,6 +92,19 @@ struct CommitArgs {
   char* next_hidden;           // [B][hd], nullable
 };
 hipError_t launch_commit(const CommitArgs& a, int B, hipStream_t s);
+
+// ---- rotary embedding of the tree tokens ----------------------------------------------------
+struct RopeArgs {
+  const void* q;            // [B][Hq][T][D]
+  void* q_rot;              // [B][Hq][T][D], written
+  void* kc;                 // [B][Hkv][lcap][D], tree rows rotated in place
+  const int32_t* prefix_len;
+  const int32_t* pos;       // [B][T]
+  float base;
+  int B, Hq, Hkv, T, D, Lmax;
+  long lcap;
+};
+hipError_t launch_rope_tree(const RopeArgs& a, int dtype, hipStream_t s);
 
 // ---- measurement --------------------------------------------------------------------------
 hipError_t launch_stream_read(const void* buf, long n16, uint32_t* sink, hipStream_t s);

@@ -117,6 +117,14 @@ def test_invalid_arguments_fail_before_any_launch(m):
     assert L.commit_accepted(*ca, 1, 4, 64, 4, *rest) == -2        # 4 bf16 = 8 bytes per row
     assert L.commit_accepted(*ca, 1, 4, 5, 128, *rest) == -2       # lcap < T
     assert L.commit_accepted(*ca, 1, 4, 64, 128, p, p, p, p, p, p, 64, None, None) == -1
+    ra = [p, p, p, 1, p, 10, 100, p, p]                         # q .. position_ids
+    assert L.tree_attention_rope(*ra, 1.0, 1, 4, 4, 9, 64, 0.0, p, p, 1 << 20, None) == -1
+    assert L.tree_attention_rope(*ra, 10000.0, 1, 4, 3, 9, 64, 0.0, p, p, 1 << 20, None) == -2
+    assert L.tree_attention_rope(*ra, 10000.0, 1, 4, 4, 9, 64, 0.0, p, p, 16, None) == -5
+    assert L.tree_attention_rope(p, p, p, 1, p, 10, 100, p, None, 10000.0, 1, 4, 4, 9, 64, 0.0,
+                                 p, p, 1 << 20, None) == -1
+    assert L.tree_attention_rope_workspace(1, 4, 4, 9, 64, 10) > \
+        L.tree_attention_workspace(1, 4, 4, 9, 64, 10)
     assert L.medusa_stream_read(p, 24, p, None) == -2
     assert L.medusa_stream_read(p, 0, p, None) == -2
     assert L.medusa_stream_read(None, 32, p, None) == -1
