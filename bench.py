@@ -303,6 +303,15 @@ def main():
     else:
         att["valu_frac"] = round(att["TFLOP/s"] / FP32_VALU_PEAK_TFLOPS, 4)
 
+    # host-side construction of this workload's sparse tree from per-head rank accuracies
+    # (the synthetic 60 % / 80 % model), for the record: it runs once per model, not per step
+    acc = np.array([[0.6 * (r + 1) ** -2.35 for r in range(cfg.topk)]] * cfg.K)
+    n_nodes = T - 1
+    t_sp = time.perf_counter()
+    for _ in range(20):
+        _, exp_len = m.sparse_tree(acc, min(n_nodes, 4095))
+    sparse_us = (time.perf_counter() - t_sp) / 20 * 1e6
+
     # greedy (temperature 0) for context: shorter run
     t0g = None
     if cfg.temps[0] == 0.0 and temperature != 0.0:
@@ -371,7 +380,9 @@ def main():
         "kernels": kernels,
         "step_time_warm": warm,
         "step_time_mall_flushed": cold,
-        "tree": {"ancestors_or_self": anc, "internal_rows": n_int},
+        "tree": {"ancestors_or_self": anc, "internal_rows": n_int,
+                 "sparse_tree_host_us": round(sparse_us, 1),
+                 "sparse_tree_expected_accept_length": round(exp_len, 4)},
         "greedy": t0g,
     }
     print(json.dumps(rec), flush=True)

@@ -299,6 +299,26 @@ int commit_accepted(const medusa_tree* tree, int B, const int32_t* best_candidat
                     const void* hidden, int hidden_size, void* next_hidden, void* stream);
 
 /* ---------------------------------------------------------------------------------------- *
+ * 6. Sparse candidate tree (host)
+ * ---------------------------------------------------------------------------------------- */
+
+/*
+ * The N-node choice list of largest expected accept length (Ultralytics page, tree-attention
+ * section: a sparse tree of the most accurate combinations beats a dense one several times its
+ * size; Wiblog page, heads section: per-head top-1 / top-5 accuracy).  accuracy [K][topk] (host
+ * fp64, each in [0, 1]): probability that head k's rank-r candidate is the right token, taken
+ * independent across heads.  Then E[accept length] = sum over nodes of prod_k accuracy[k][r_k]
+ * and the best tree is the N most likely nodes, ties broken by depth and then rank tuple
+ * (node probabilities are products in depth order, fp64).  choices [N][K] (host int32) receives
+ * the rank tuples in node order (depth, then rank tuple), -1 padded: a medusa_choices list for
+ * build_tree with max_depth = K.  *expected_accept_length (nullable) receives the expectation,
+ * summed in node order.  Host only; no device work.
+ * Limits: 1 <= K <= 8, 1 <= topk <= 64, 1 <= N <= min(4095, nodes of the full tree).
+ */
+int medusa_sparse_tree(const double* accuracy, int K, int topk, int N, int32_t* choices,
+                       double* expected_accept_length);
+
+/* ---------------------------------------------------------------------------------------- *
  * Measurement hook (not part of the method)
  * ---------------------------------------------------------------------------------------- */
 

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     pack_weights,
     medusa_heads_workspace,
     set_kernel_events,
+    sparse_tree,
     stream_read,
     tree_attention,
     tree_attention_rope,

@@ -1,4 +1,5 @@
-"""ctypes binding of libmedusa_hip.so.  Argument marshalling only: every step runs in HIP kernels.
+"""ctypes binding of libmedusa_hip.so.  Argument marshalling only: every step runs in the library
+(HIP kernels; the static tree and the sparse-tree choice are its host code).
 
 Tensors are torch tensors on the current HIP device (bf16 tensors may be torch.bfloat16 or
 int16/uint16 bit patterns); the functions pass their data pointers and the current stream to the
@@ -8,6 +9,7 @@ C ABI declared in include/medusa.h and raise MedusaError on a non-zero status.
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,7 +41,7 @@ EXPORTS = ["medusa_last_error", "medusa_heads_workspace", "medusa_heads", "medus
            "typical_accept_workspace", "typical_accept", "medusa_set_kernel_events",
            "medusa_heads_packed", "medusa_packed_weight_bytes", "medusa_pack_weights",
            "medusa_stream_read", "commit_accepted", "tree_attention_rope_workspace",
-           "tree_attention_rope"]
+           "tree_attention_rope", "medusa_sparse_tree"]
 
 KERNELS = ["heads_w1", "heads_w2", "topk", "tree_gather", "attention", "attn_combine", "accept",
            "commit", "rope"]
@@ -91,6 +93,8 @@ def load():
     L.tree_attention_rope.restype = i
     L.tree_attention_rope.argtypes = [vp, vp, vp, i, vp, i, l, vp, vp, f, i, i, i, i, i, f, vp,
                                       vp, sz, vp]
+    L.medusa_sparse_tree.restype = i
+    L.medusa_sparse_tree.argtypes = [vp, i, i, i, vp, vp]
     L.commit_accepted.restype = i
     L.commit_accepted.argtypes = [ctypes.POINTER(medusa_tree), i, vp, vp, vp, vp, vp, vp, i, i, l,
                                   i, vp, vp, vp, vp, vp, vp, i, vp, vp]
@@ -281,6 +285,18 @@ def commit_accepted(tree, best_candidate, accept_length, tokens, next_token, k_c
                                   _ptr(prefix_len), _ptr(new_prefix_len), _ptr(out_tokens),
                                   _ptr(out_count), _ptr(new_root), _ptr(hidden), hd,
                                   _ptr(next_hidden), _stream(stream)))
+
+
+def sparse_tree(accuracy, N):
+    """The N-node choice list of largest expected accept length for per-head rank accuracies
+    accuracy [K][topk] (host).  Returns (choices as lists of ranks in node order, expectation)."""
+    acc = np.ascontiguousarray(accuracy, dtype=np.float64)
+    K, topk = acc.shape
+    out = np.empty((N, K), np.int32)
+    e = ctypes.c_double()
+    _check(load().medusa_sparse_tree(acc.ctypes.data, K, topk, N, out.ctypes.data,
+                                     ctypes.byref(e)))
+    return [[int(r) for r in row if r >= 0] for row in out], e.value
 
 
 # ---------------------------------------------------------------------------------------------

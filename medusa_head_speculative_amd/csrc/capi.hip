@@ -450,6 +450,27 @@ int commit_accepted(const medusa_tree* tree, int B, const int32_t* best_candidat
   return launched(medusa::launch_commit(a, B, static_cast<hipStream_t>(stream)), "commit_accepted");
 }
 
+// ---- sparse candidate tree (host) ------------------------------------------------------------
+int medusa_sparse_tree(const double* accuracy, int K, int topk, int N, int32_t* choices,
+                       double* expected_accept_length) {
+  if (!accuracy || !choices) return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
+  if (K < 1 || K > 8) return fail(MEDUSA_ERR_SHAPE, "K = %d, need 1..8", K);
+  if (topk < 1 || topk > 64) return fail(MEDUSA_ERR_SHAPE, "topk = %d, need 1..64", topk);
+  double total = 0.0, level = 1.0;                 // nodes of the full tree, capped
+  for (int d = 0; d < K && total <= 4095.0; ++d) {
+    level *= topk;
+    total += level;
+  }
+  if (N < 1 || N > 4095 || N > total) return fail(MEDUSA_ERR_SHAPE, "N = %d, need 1..min(4095, nodes of the full tree)", N);
+  for (long i = 0; i < static_cast<long>(K) * topk; ++i)
+    if (!(accuracy[i] >= 0.0 && accuracy[i] <= 1.0))
+      return fail(MEDUSA_ERR_ARG, "accuracy[%ld] = %g is not in [0, 1]", i, accuracy[i]);
+  const double e = medusa::build_sparse_tree(accuracy, K, topk, N, choices);
+  if (expected_accept_length) *expected_accept_length = e;
+  g_err[0] = '\0';
+  return MEDUSA_OK;
+}
+
 // ---- measurement hook ------------------------------------------------------------------------
 int medusa_set_kernel_events(int which, void* before, void* after) {
   if (which < 0 || which >= medusa::kKernelCount) return fail(MEDUSA_ERR_ARG, "kernel id %d", which);

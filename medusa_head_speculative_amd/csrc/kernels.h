@@ -106,6 +106,9 @@ struct RopeArgs {
 };
 hipError_t launch_rope_tree(const RopeArgs& a, int dtype, hipStream_t s);
 
+// ---- sparse candidate tree (host) ----------------------------------------------------------
+double build_sparse_tree(const double* acc, int K, int topk, int N, int32_t* choices);
+
 // ---- measurement --------------------------------------------------------------------------
 hipError_t launch_stream_read(const void* buf, long n16, uint32_t* sink, hipStream_t s);
 
