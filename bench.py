@@ -303,6 +303,40 @@ def main():
     else:
         att["valu_frac"] = round(att["TFLOP/s"] / FP32_VALU_PEAK_TFLOPS, 4)
 
+    # head variant: two residual blocks opened by LayerNorm at this workload's shape (random
+    # weights drawn on the device), timed as whole medusa_heads_ex calls
+    nbx = 2
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    std = cfg.Hd ** -0.5
+    def rnd(*shape, scale=std, shift=0.0):
+        return (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * scale + shift).to(tdt)
+    w1x = rnd(cfg.K * nbx, cfg.Hd, cfg.Hd)
+    b1x, gx, bx = rnd(cfg.K, nbx, cfg.Hd), rnd(cfg.K, nbx, cfg.Hd, scale=0.1, shift=1.0), rnd(cfg.K, nbx, cfg.Hd, scale=0.1)
+    packed = cfg.dtype == "bf16"
+    if packed:
+        w1x = m.pack_weights(w1x)
+    else:
+        w1x = w1x.view(cfg.K, nbx, cfg.Hd, cfg.Hd)
+    wsx = m.workspace(m.medusa_heads_ex_workspace(cfg.B, cfg.Hd, cfg.V, cfg.K, nbx, True, cfg.topk))
+    idsx = torch.zeros((cfg.B, cfg.K, cfg.topk), dtype=torch.int32, device="cuda")
+    hx = h
+    xev = make_events(20)
+    for i in range(22):
+        if i >= 2:
+            xev[i - 2][0].record(stream)
+        m.medusa_heads_ex(hx, w1x, b1x, w2, cfg.V, cfg.K, nbx, cfg.topk, idsx, wsx, ln_gamma=gx,
+                          ln_beta=bx, packed=packed)
+        if i >= 2:
+            xev[i - 2][1].record(stream)
+    torch.cuda.synchronize()
+    x_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in xev]))
+    x_bytes = cfg.K * (nbx * cfg.Hd * cfg.Hd + cfg.V * cfg.Hd) * cfg.esize
+    head_variant = {"n_blocks": nbx, "layernorm": True, "ms": round(x_ms, 5), "alg_bytes": x_bytes,
+                    "GB/s": round(x_bytes / (x_ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(x_bytes / (x_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del w1x, b1x, gx, bx, wsx
+
     # host-side construction of this workload's sparse tree from per-head rank accuracies
     # (the synthetic 60 % / 80 % model), for the record: it runs once per model, not per step
     acc = np.array([[0.6 * (r + 1) ** -2.35 for r in range(cfg.topk)]] * cfg.K)
@@ -378,6 +412,7 @@ def main():
         "step_alg_bytes": total_bytes,
         "step_GB/s": round(total_bytes * steps_per_s / 1e9, 1),
         "kernels": kernels,
+        "heads_variant": head_variant,
         "step_time_warm": warm,
         "step_time_mall_flushed": cold,
         "tree": {"ancestors_or_self": anc, "internal_rows": n_int,

@@ -116,7 +116,34 @@ int medusa_heads_packed(const void* h, const void* w1_packed, const void* b1,
                         float* logits, int32_t* topk_ids, float* topk_logits, void* workspace,
                         size_t workspace_bytes, void* stream);
 
-/* Bytes of the packed form of K bf16 matrices of [rows, hidden] (0 on invalid sizes). */
+/*
+ * Heads of n_blocks residual blocks each, optionally opened by LayerNorm (Wiblog page, heads
+ * section: a head is one or more residual blocks, of LayerNorm and a feed-forward network,
+ * followed by a linear layer; the block itself is Ultralytics' fully connected layer with SiLU
+ * and a residual connection).  Per head k, starting from x = h:
+ *     for j in 0 .. n_blocks-1:  x <- x + SiLU(W1[k][j] n(x) + b1[k][j])
+ *     logits[b][k][:] = W2[k] x,   then the per-head top-k as medusa_heads,
+ * with n(x) = x when ln_gamma and ln_beta are NULL, else the LayerNorm over the hidden
+ * dimension, (x - mean) / sqrt(var + ln_eps) * ln_gamma[k][j] + ln_beta[k][j] (var the mean
+ * squared deviation, statistics in fp32).  x is carried in fp32 between blocks.
+ *   w1     [K][n_blocks][hidden][hidden] dtype, or with packed = 1 (bf16 only) the
+ *          medusa_pack_weights form of that tensor taken as K * n_blocks matrices
+ *   b1     [K][n_blocks][hidden] dtype;  ln_gamma, ln_beta [K][n_blocks][hidden] dtype or NULL
+ *   w2     [K][vocab][hidden] dtype, or its packed form (packed = 1)
+ * Everything else as medusa_heads; n_blocks = 1 without LayerNorm is exactly medusa_heads
+ * (packed = 0) or medusa_heads_packed (packed = 1).  The workspace query takes layernorm = 0/1.
+ * Limits: those of medusa_heads, 1 <= n_blocks <= 8, ln_eps > 0.
+ */
+size_t medusa_heads_ex_workspace(int B, int hidden, long vocab, int K, int n_blocks, int layernorm,
+                                 int topk);
+int medusa_heads_ex(const void* h, const void* w1, const void* b1, const void* ln_gamma,
+                    const void* ln_beta, float ln_eps, const void* w2, int dtype, int packed,
+                    int B, int hidden, long vocab, int K, int n_blocks, int topk, float* logits,
+                    int32_t* topk_ids, float* topk_logits, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Bytes of the packed form of K bf16 matrices of [rows, hidden] (0 on invalid sizes;
+   limits as medusa_pack_weights). */
 size_t medusa_packed_weight_bytes(int K, long rows, int hidden);
 
 /*
@@ -126,7 +153,9 @@ size_t medusa_packed_weight_bytes(int K, long rows, int hidden);
  * follow one another (1 KB per tile), rows past `rows` zero-filled:
  *   packed[kb][k][tile][lane][e] = w[k][16 tile + lane % 16][32 kb + 8 (lane / 16) + e],
  * kb < hidden / 32, tile < ceil(rows / 16), lane < 64, e < 8.
- * Done once per model, outside the decode loop.  Limits as medusa_heads.
+ * Done once per model, outside the decode loop.
+ * Limits: 1 <= K <= 64 (K heads, or K * n_blocks stacked block weights for medusa_heads_ex),
+ *         1 <= rows < 2^31, hidden a multiple of 32 in 32..16384.
  */
 int medusa_pack_weights(const void* w, int K, long rows, int hidden, void* packed, void* stream);
 

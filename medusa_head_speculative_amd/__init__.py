@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     commit_accepted,
     load,
     medusa_heads,
+    medusa_heads_ex,
+    medusa_heads_ex_workspace,
     medusa_heads_packed,
     pack_weights,
     medusa_heads_workspace,

@@ -41,7 +41,8 @@ EXPORTS = ["medusa_last_error", "medusa_heads_workspace", "medusa_heads", "medus
            "typical_accept_workspace", "typical_accept", "medusa_set_kernel_events",
            "medusa_heads_packed", "medusa_packed_weight_bytes", "medusa_pack_weights",
            "medusa_stream_read", "commit_accepted", "tree_attention_rope_workspace",
-           "tree_attention_rope", "medusa_sparse_tree"]
+           "tree_attention_rope", "medusa_sparse_tree", "medusa_heads_ex_workspace",
+           "medusa_heads_ex"]
 
 KERNELS = ["heads_w1", "heads_w2", "topk", "tree_gather", "attention", "attn_combine", "accept",
            "commit", "rope"]
@@ -93,6 +94,11 @@ def load():
     L.tree_attention_rope.restype = i
     L.tree_attention_rope.argtypes = [vp, vp, vp, i, vp, i, l, vp, vp, f, i, i, i, i, i, f, vp,
                                       vp, sz, vp]
+    L.medusa_heads_ex_workspace.restype = sz
+    L.medusa_heads_ex_workspace.argtypes = [i, i, l, i, i, i, i]
+    L.medusa_heads_ex.restype = i
+    L.medusa_heads_ex.argtypes = [vp, vp, vp, vp, vp, f, vp, i, i, i, i, l, i, i, i, vp, vp, vp,
+                                  vp, sz, vp]
     L.medusa_sparse_tree.restype = i
     L.medusa_sparse_tree.argtypes = [vp, i, i, i, vp, vp]
     L.commit_accepted.restype = i
@@ -170,6 +176,24 @@ def medusa_heads_packed(h, w1_packed, b1, w2_packed, vocab, K, topk, topk_ids, w
 
 
 # ---------------------------------------------------------------------------------------------
+def medusa_heads_ex_workspace(B, hidden, vocab, K, n_blocks, layernorm, topk):
+    return load().medusa_heads_ex_workspace(B, hidden, vocab, K, n_blocks, 1 if layernorm else 0,
+                                            topk)
+
+
+def medusa_heads_ex(h, w1, b1, w2, vocab, K, n_blocks, topk, topk_ids, ws, ln_gamma=None,
+                    ln_beta=None, ln_eps=1e-5, packed=False, logits=None, topk_logits=None,
+                    stream=None):
+    """Heads of n_blocks residual blocks (optionally with LayerNorm).  w1 [K, n_blocks, Hd, Hd]
+    (or pack_weights of its [K * n_blocks, Hd, Hd] view with packed=True), b1 [K, n_blocks, Hd],
+    ln_gamma / ln_beta [K, n_blocks, Hd] or None, w2 [K, V, Hd] (or packed)."""
+    B, hd = h.shape
+    _check(load().medusa_heads_ex(_ptr(h), _ptr(w1), _ptr(b1), _ptr(ln_gamma), _ptr(ln_beta),
+                                  ln_eps, _ptr(w2), dtype_code(h), 1 if packed else 0, B, hd,
+                                  vocab, K, n_blocks, topk, _ptr(logits), _ptr(topk_ids),
+                                  _ptr(topk_logits), _ptr(ws), ws.numel(), _stream(stream)))
+
+
 def _choices_array(choices, max_depth=None):
     import numpy as np
     md = max_depth or max(len(c) for c in choices)

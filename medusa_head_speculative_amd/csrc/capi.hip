@@ -179,8 +179,39 @@ int medusa_heads(const void* h, const void* w1, const void* b1, const void* w2, 
                   "medusa_heads");
 }
 
+size_t medusa_heads_ex_workspace(int B, int hidden, long vocab, int K, int n_blocks, int layernorm,
+                                 int topk) {
+  if (heads_shape(B, hidden, vocab, K, topk) != MEDUSA_OK || n_blocks < 1 || n_blocks > 8) return 0;
+  return medusa::heads_ws_layout(B, hidden, vocab, K, topk, n_blocks, layernorm ? 1 : 0).total;
+}
+
+int medusa_heads_ex(const void* h, const void* w1, const void* b1, const void* ln_gamma,
+                    const void* ln_beta, float ln_eps, const void* w2, int dtype, int packed,
+                    int B, int hidden, long vocab, int K, int n_blocks, int topk, float* logits,
+                    int32_t* topk_ids, float* topk_logits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_DTYPE, "dtype = %d", dtype);
+  if (packed && dtype != MEDUSA_BF16) return fail(MEDUSA_ERR_DTYPE, "packed weights are bf16");
+  if (!h || !w1 || !b1 || !w2 || !topk_ids) return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
+  if ((ln_gamma == nullptr) != (ln_beta == nullptr))
+    return fail(MEDUSA_ERR_ARG, "give both ln_gamma and ln_beta or neither");
+  if (ln_gamma && !(ln_eps > 0.f && std::isfinite(ln_eps))) return fail(MEDUSA_ERR_ARG, "ln_eps = %g, need > 0", ln_eps);
+  int rc = heads_shape(B, hidden, vocab, K, topk);
+  if (rc) return rc;
+  if (n_blocks < 1 || n_blocks > 8) return fail(MEDUSA_ERR_SHAPE, "n_blocks = %d, need 1..8", n_blocks);
+  const size_t need = medusa::heads_ws_layout(B, hidden, vocab, K, topk, n_blocks, ln_gamma ? 1 : 0).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if ((rc = check_pending())) return rc;
+  return launched(medusa::launch_heads_ex(h, w1, b1, ln_gamma, ln_beta, ln_eps, w2, dtype, packed ? 1 : 0,
+                                          n_blocks, B, hidden, vocab, K, topk, logits, topk_ids,
+                                          topk_logits, static_cast<char*>(workspace),
+                                          static_cast<hipStream_t>(stream)),
+                  "medusa_heads_ex");
+}
+
 size_t medusa_packed_weight_bytes(int K, long rows, int hidden) {
-  if (K < 1 || K > 8 || rows < 1 || rows >= (1l << 31) || hidden < 32 || hidden > 16384 || hidden % 32)
+  if (K < 1 || K > 64 || rows < 1 || rows >= (1l << 31) || hidden < 32 || hidden > 16384 || hidden % 32)
     return 0;
   return medusa::packed_weight_bytes(K, rows, hidden);
 }

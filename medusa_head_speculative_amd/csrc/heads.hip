@@ -33,7 +33,16 @@ struct HeadsEpi {
   float* r_out;           // [B][K][hd] fp32          (mode 0)
   uint16_t* xs;           // [K][2B][hd] bf16         (mode 0, bf16 path): hi(r) rows, then lo(r)
   float* logits;          // [B][K][rows] fp32        (mode 1)
+  // heads of several residual blocks (zero values: one block, residual from h, x shared)
+  int nb;                 // blocks per head; the weights of head k, block blk are weight head
+  int blk;                //   k * max(nb, 1) + blk of the [K * nb] stacked / packed tensors
+  const float* r_res;     // [B][K][hd] fp32 residual input (mode 0), NULL: h
+  int x_per_head;         // the vector operand is per head ([K][ncols][hd]) in mode 0 too
 };
+
+__device__ __forceinline__ int weight_head(const HeadsEpi& ep, int k) {
+  return k * (ep.nb > 1 ? ep.nb : 1) + ep.blk;
+}
 
 __device__ __forceinline__ float load_elem(const void* p, int dtype, long i) {
   return dtype == 0 ? static_cast<const float*>(p)[i] : bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
@@ -43,8 +52,10 @@ __device__ __forceinline__ float load_elem(const void* p, int dtype, long i) {
 __device__ __forceinline__ void heads_epilogue(const HeadsEpi& ep, int k, long row, int b, float y) {
   if (ep.mode == 0) {
     const int i = static_cast<int>(row);
-    const float u = y + load_elem(ep.b1, ep.dtype, static_cast<long>(k) * ep.hd + i);
-    const float r = load_elem(ep.h, ep.dtype, static_cast<long>(b) * ep.hd + i) + u / (1.0f + expf(-u));
+    const float u = y + load_elem(ep.b1, ep.dtype, static_cast<long>(weight_head(ep, k)) * ep.hd + i);
+    const float x = ep.r_res ? ep.r_res[(static_cast<long>(b) * ep.K + k) * ep.hd + i]
+                             : load_elem(ep.h, ep.dtype, static_cast<long>(b) * ep.hd + i);
+    const float r = x + u / (1.0f + expf(-u));
     ep.r_out[(static_cast<long>(b) * ep.K + k) * ep.hd + i] = r;
     if (ep.xs) {
       // the vocab projection's vector operand: hi(r) and lo(r) = r - hi(r) as bf16 rows
@@ -99,9 +110,10 @@ __global__ __launch_bounds__(256) void heads_gemv_bf16(const uint16_t* __restric
   for (int t = 0; t < TPW; ++t) {
     long r = row0 + t * 16 + n;
     if (r > ep.rows - 1) r = ep.rows - 1;          // ragged tail: valid address, result dropped
-    wrow[t] = W + (static_cast<long>(k) * ep.rows + r) * hd + g * 8;
+    wrow[t] = W + (static_cast<long>(weight_head(ep, k)) * ep.rows + r) * hd + g * 8;
   }
-  const uint16_t* xp = n < ncols ? xsrc + (static_cast<long>(k) * ncols * ep.mode + n) * hd + g * 8
+  const int xph = ep.mode == 1 || ep.x_per_head;
+  const uint16_t* xp = n < ncols ? xsrc + (static_cast<long>(k) * ncols * xph + n) * hd + g * 8
                                  : nullptr;
 
   f32x4_t acc[TPW];
@@ -176,8 +188,9 @@ __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restr
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const long ntiles = (ep.rows + 15) >> 4;
-  const long G = ntiles * ep.K;
+  const long G = ntiles * ep.K * (ep.nb > 1 ? ep.nb : 1);   // tiles of all packed weight heads
   const long per_head = (ntiles + TPW - 1) / TPW;      // work items per head
+  const int xph = ep.mode == 1 || ep.x_per_head;
   const int hd = ep.hd;
   const int nkb = hd >> 5;
   const long kbstride = G * 512;                        // elements from block kb to kb + 1
@@ -208,9 +221,9 @@ __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restr
     for (int t = 0; t < TPW; ++t) {
       long tt = t0 + t;
       if (tt > ntiles - 1) tt = ntiles - 1;             // ragged: valid address, result dropped
-      ap[t] = Wp + (static_cast<long>(k) * ntiles + tt) * 512 + static_cast<long>(kb0) * kbstride + lane * 8;
+      ap[t] = Wp + (static_cast<long>(weight_head(ep, k)) * ntiles + tt) * 512 + static_cast<long>(kb0) * kbstride + lane * 8;
     }
-    const uint16_t* xp = n < ncols ? xsrc + (static_cast<long>(k) * ncols * ep.mode + n) * hd + g * 8
+    const uint16_t* xp = n < ncols ? xsrc + (static_cast<long>(k) * ncols * xph + n) * hd + g * 8
                                    : nullptr;
 
     f32x4_t acc[TPW];
@@ -308,7 +321,7 @@ __global__ __launch_bounds__(256) void heads_gemv_f32(const float* __restrict__ 
   const int k = blockIdx.y;
   if (row >= ep.rows) return;
   const int hd = ep.hd, B = ep.B;
-  const float* w = W + (static_cast<long>(k) * ep.rows + row) * hd;
+  const float* w = W + (static_cast<long>(weight_head(ep, k)) * ep.rows + row) * hd;
   const float* xk = x + static_cast<long>(k) * x_kstride;
   float acc[8];
 #pragma unroll
@@ -416,14 +429,71 @@ __global__ __launch_bounds__(64) void topk_merge(const uint64_t* __restrict__ pa
 }
 
 // ------------------------------------------------------------------------------------------
+// LayerNorm of a block's input (heads whose residual blocks start with LayerNorm)
+// ------------------------------------------------------------------------------------------
+// One work-group per (sequence, head): mean and mean squared deviation over the hidden dimension
+// in fp32 (two passes over the row, which stays in cache, fixed-order sums), then
+// (x - mean) / sqrt(var + eps) * gamma + beta as the next layer's vector operand: hi/lo bf16
+// rows of xs (matrix-core path) or fp32 rows of xn (fp32 path).
+__device__ __forceinline__ float block_sum256(float v, float* s_red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float t = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  __syncthreads();
+  return t;
+}
+
+__global__ __launch_bounds__(256) void heads_layernorm(const void* h, const float* r_in, int dtype,
+                                                       const void* gamma, const void* beta, float eps,
+                                                       int B, int K, int hd, int wh_mul, int blk,
+                                                       uint16_t* xs, float* xn) {
+  __shared__ float s_red[4];
+  const int b = blockIdx.x, k = blockIdx.y;
+  auto xval = [&](int i) {
+    return r_in ? r_in[(static_cast<long>(b) * K + k) * hd + i]
+                : load_elem(h, dtype, static_cast<long>(b) * hd + i);
+  };
+  float sum = 0.f;
+  for (int i = threadIdx.x; i < hd; i += 256) sum += xval(i);
+  const float mean = block_sum256(sum, s_red) / static_cast<float>(hd);
+  float sq = 0.f;
+  for (int i = threadIdx.x; i < hd; i += 256) {
+    const float d = xval(i) - mean;
+    sq = fmaf(d, d, sq);
+  }
+  const float var = block_sum256(sq, s_red) / static_cast<float>(hd);
+  const float rstd = 1.0f / sqrtf(var + eps);
+  const long wb = static_cast<long>(k * wh_mul + blk) * hd;
+  for (int i = threadIdx.x; i < hd; i += 256) {
+    const float y = (xval(i) - mean) * rstd * load_elem(gamma, dtype, wb + i) + load_elem(beta, dtype, wb + i);
+    if (xs) {
+      const uint16_t hi = f32_to_bf16_rne(y);
+      const uint16_t lo = f32_to_bf16_rne(y - bf16_to_f32(hi));
+      uint16_t* base = xs + static_cast<long>(k) * 2 * B * hd + i;
+      base[static_cast<long>(b) * hd] = hi;
+      base[static_cast<long>(B + b) * hd] = lo;
+    } else {
+      xn[(static_cast<long>(b) * K + k) * hd + i] = y;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // launcher
 // ------------------------------------------------------------------------------------------
-HeadsWs heads_ws_layout(int B, int hd, long V, int K, int topk) {
+HeadsWs heads_ws_layout(int B, int hd, long V, int K, int topk, int nb, int ln) {
   HeadsWs w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
-  w.r = take(sizeof(float) * B * K * hd);
-  w.xs = take(sizeof(uint16_t) * static_cast<size_t>(K) * 2 * B * hd);
+  const size_t rbytes = sizeof(float) * B * K * hd;
+  const size_t xbytes = sizeof(uint16_t) * static_cast<size_t>(K) * 2 * B * hd;
+  w.r = take(rbytes);
+  w.r2 = nb > 1 ? take(rbytes) : w.r;            // block inputs and outputs alternate
+  w.xs = take(xbytes);
+  w.xs2 = nb > 1 || ln ? take(xbytes) : w.xs;
+  w.xn = ln ? take(rbytes) : 0;                   // LayerNorm output of the fp32 path
   w.logits = take(sizeof(float) * static_cast<size_t>(B) * K * V);
   const long C = (V + kTopkChunk - 1) / kTopkChunk;
   w.part = take(sizeof(uint64_t) * static_cast<size_t>(B) * K * C * topk);
@@ -503,53 +573,95 @@ static void launch_packed(int variant, const uint16_t* Wp, const uint16_t* x, in
 #undef MEDUSA_PACKED_CASE
 }
 
-hipError_t launch_heads(const void* h, const void* w1, const void* b1, const void* w2, int dtype,
-                        int packed, int B, int hd, long V, int K, int topk, float* logits,
-                        int32_t* topk_ids, float* topk_logits, char* ws, hipStream_t s) {
-  const HeadsWs L = heads_ws_layout(B, hd, V, K, topk);
-  float* r = reinterpret_cast<float*>(ws + L.r);
-  uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xs);
+hipError_t launch_heads_ex(const void* h, const void* w1, const void* b1, const void* gamma,
+                           const void* beta, float eps, const void* w2, int dtype, int packed, int nb,
+                           int B, int hd, long V, int K, int topk, float* logits, int32_t* topk_ids,
+                           float* topk_logits, char* ws, hipStream_t s) {
+  const bool ln = gamma != nullptr;
+  const HeadsWs L = heads_ws_layout(B, hd, V, K, topk, nb, ln);
+  float* rb[2] = {reinterpret_cast<float*>(ws + L.r), reinterpret_cast<float*>(ws + L.r2)};
+  uint16_t* xb[2] = {reinterpret_cast<uint16_t*>(ws + L.xs), reinterpret_cast<uint16_t*>(ws + L.xs2)};
+  float* xn = ln ? reinterpret_cast<float*>(ws + L.xn) : nullptr;
   float* lg = logits ? logits : reinterpret_cast<float*>(ws + L.logits);
   uint64_t* part = reinterpret_cast<uint64_t*>(ws + L.part);
-
-  HeadsEpi e1{0, K, hd, hd, B, b1, h, dtype, r, dtype == 1 ? xs : nullptr, nullptr};
-  HeadsEpi e2{1, K, V, hd, B, nullptr, nullptr, dtype, nullptr, nullptr, lg};
   const uint16_t* hb = static_cast<const uint16_t*>(h);
-  if (dtype == 1 && packed) {
-    static const int v1 = variant_from_env("MEDUSA_W1_VARIANT", kDefaultW1Variant);
-    static const int v2_env = variant_from_env("MEDUSA_W2_VARIANT", -1);
-    const int v2 = v2_env >= 0 ? v2_env : default_w2_variant(B);
+  static const int v1 = variant_from_env("MEDUSA_W1_VARIANT", kDefaultW1Variant);
+  static const int v2_env = variant_from_env("MEDUSA_W2_VARIANT", -1);
+
+  // block j reads its input from h (j = 0) or r buffer `cur`, writes r buffer `cur ^ 1` (0 for
+  // j = 0) and the next layer's hi/lo operand into the xs buffer it does not read
+  int cur = -1, xcur = -1;
+  for (int j = 0; j < nb; ++j) {
+    const int out = cur < 0 ? 0 : cur ^ 1;
+    HeadsEpi e1{0, K, hd, hd, B, b1, h, dtype, rb[out], nullptr, nullptr, nb, j,
+                cur < 0 ? nullptr : rb[cur], 0};
+    const uint16_t* xop = hb;          // the layer's vector operand (bf16 paths)
+    int ncols = B;
+    const float* xf = static_cast<const float*>(h);   // (fp32 path)
+    long xf_b = hd, xf_k = 0;
+    if (ln) {
+      const int xl = xcur == 0 ? 1 : 0;
+      heads_layernorm<<<dim3(B, K), 256, 0, s>>>(h, cur < 0 ? nullptr : rb[cur], dtype, gamma, beta,
+                                                 eps, B, K, hd, nb, j, dtype == 1 ? xb[xl] : nullptr, xn);
+      xop = xb[xl];
+      ncols = 2 * B;
+      e1.x_per_head = 1;
+      xcur = xl;
+      xf = xn;
+      xf_b = static_cast<long>(K) * hd;
+      xf_k = hd;
+    } else if (j > 0) {
+      xop = xb[xcur];
+      ncols = 2 * B;
+      e1.x_per_head = 1;
+      xf = rb[cur];
+      xf_b = static_cast<long>(K) * hd;
+      xf_k = hd;
+    }
+    const int xo = xcur == 0 ? 1 : 0;  // the operand written for the next layer
+    if (dtype == 1) e1.xs = xb[xo];
     hook_before(K_HEADS_W1, s);
-    launch_packed(v1, static_cast<const uint16_t*>(w1), hb, B, e1, s);
+    if (dtype == 1 && packed) {
+      launch_packed(v1, static_cast<const uint16_t*>(w1), xop, ncols, e1, s);
+    } else if (dtype == 1) {
+      constexpr int TPW1 = 2;
+      heads_gemv_bf16<TPW1><<<dim3((hd + 16 * TPW1 - 1) / (16 * TPW1), K), 256, 0, s>>>(
+          static_cast<const uint16_t*>(w1), xop, ncols, e1);
+    } else {
+      heads_gemv_f32<<<dim3((hd + 3) / 4, K), 256, 0, s>>>(static_cast<const float*>(w1), xf, xf_b,
+                                                           xf_k, e1);
+    }
     hook_after(K_HEADS_W1, s);
-    hook_before(K_HEADS_W2, s);
-    launch_packed(v2, static_cast<const uint16_t*>(w2), xs, 2 * B, e2, s);
-    hook_after(K_HEADS_W2, s);
-  } else if (dtype == 1) {
-    constexpr int TPW1 = 2, TPW2 = 2;
-    hook_before(K_HEADS_W1, s);
-    heads_gemv_bf16<TPW1><<<dim3((hd + 16 * TPW1 - 1) / (16 * TPW1), K), 256, 0, s>>>(
-        static_cast<const uint16_t*>(w1), hb, B, e1);
-    hook_after(K_HEADS_W1, s);
-    hook_before(K_HEADS_W2, s);
-    heads_gemv_bf16<TPW2><<<dim3((V + 16 * TPW2 - 1) / (16 * TPW2), K), 256, 0, s>>>(
-        static_cast<const uint16_t*>(w2), xs, 2 * B, e2);
-    hook_after(K_HEADS_W2, s);
-  } else {
-    hook_before(K_HEADS_W1, s);
-    heads_gemv_f32<<<dim3((hd + 3) / 4, K), 256, 0, s>>>(static_cast<const float*>(w1),
-                                                         static_cast<const float*>(h), hd, 0, e1);
-    hook_after(K_HEADS_W1, s);
-    hook_before(K_HEADS_W2, s);
-    heads_gemv_f32<<<dim3((V + 3) / 4, K), 256, 0, s>>>(static_cast<const float*>(w2), r,
-                                                        static_cast<long>(K) * hd, hd, e2);
-    hook_after(K_HEADS_W2, s);
+    cur = out;
+    xcur = xo;
   }
+
+  HeadsEpi e2{1, K, V, hd, B, nullptr, nullptr, dtype, nullptr, nullptr, lg, 0, 0, nullptr, 1};
+  hook_before(K_HEADS_W2, s);
+  if (dtype == 1 && packed) {
+    const int v2 = v2_env >= 0 ? v2_env : default_w2_variant(B);
+    launch_packed(v2, static_cast<const uint16_t*>(w2), xb[xcur], 2 * B, e2, s);
+  } else if (dtype == 1) {
+    constexpr int TPW2 = 2;
+    heads_gemv_bf16<TPW2><<<dim3((V + 16 * TPW2 - 1) / (16 * TPW2), K), 256, 0, s>>>(
+        static_cast<const uint16_t*>(w2), xb[xcur], 2 * B, e2);
+  } else {
+    heads_gemv_f32<<<dim3((V + 3) / 4, K), 256, 0, s>>>(static_cast<const float*>(w2), rb[cur],
+                                                        static_cast<long>(K) * hd, hd, e2);
+  }
+  hook_after(K_HEADS_W2, s);
   hook_before(K_TOPK, s);
   topk_chunks<<<dim3(L.chunks, B * K), kTopkThreads, 0, s>>>(lg, V, topk, L.chunks, part);
   topk_merge<<<B * K, 64, 0, s>>>(part, topk, L.chunks, topk_ids, topk_logits);
   hook_after(K_TOPK, s);
   return hipGetLastError();
+}
+
+hipError_t launch_heads(const void* h, const void* w1, const void* b1, const void* w2, int dtype,
+                        int packed, int B, int hd, long V, int K, int topk, float* logits,
+                        int32_t* topk_ids, float* topk_logits, char* ws, hipStream_t s) {
+  return launch_heads_ex(h, w1, b1, nullptr, nullptr, 0.f, w2, dtype, packed, 1, B, hd, V, K, topk,
+                         logits, topk_ids, topk_logits, ws, s);
 }
 
 }  // namespace medusa

@@ -24,10 +24,14 @@ inline void hook_after(int k, hipStream_t s) {
 
 // ---- heads -------------------------------------------------------------------------------
 struct HeadsWs {
-  size_t r, xs, logits, part, total;
+  size_t r, r2, xs, xs2, xn, logits, part, total;
   int chunks;
 };
-HeadsWs heads_ws_layout(int B, int hd, long V, int K, int topk);
+HeadsWs heads_ws_layout(int B, int hd, long V, int K, int topk, int nb = 1, int ln = 0);
+hipError_t launch_heads_ex(const void* h, const void* w1, const void* b1, const void* gamma,
+                           const void* beta, float eps, const void* w2, int dtype, int packed, int nb,
+                           int B, int hd, long V, int K, int topk, float* logits, int32_t* topk_ids,
+                           float* topk_logits, char* ws, hipStream_t s);
 hipError_t launch_heads(const void* h, const void* w1, const void* b1, const void* w2, int dtype,
                         int packed, int B, int hd, long V, int K, int topk, float* logits,
                         int32_t* topk_ids, float* topk_logits, char* ws, hipStream_t s);

@@ -125,6 +125,16 @@ def test_invalid_arguments_fail_before_any_launch(m):
                                  p, p, 1 << 20, None) == -1
     assert L.tree_attention_rope_workspace(1, 4, 4, 9, 64, 10) > \
         L.tree_attention_workspace(1, 4, 4, 9, 64, 10)
+    hx = [p, p, p, p, p, 1e-5, p]                                # h .. w2
+    assert L.medusa_heads_ex(*hx, 0, 1, 1, 64, 100, 1, 2, 1, None, p, None, p, 1 << 20, None) == -3
+    assert L.medusa_heads_ex(*hx, 1, 0, 1, 64, 100, 1, 9, 1, None, p, None, p, 1 << 20, None) == -2
+    assert L.medusa_heads_ex(p, p, p, p, None, 1e-5, p, 1, 0, 1, 64, 100, 1, 2, 1, None, p, None,
+                             p, 1 << 20, None) == -1
+    assert L.medusa_heads_ex(*hx[:5], 0.0, p, 1, 0, 1, 64, 100, 1, 2, 1, None, p, None, p, 1 << 20,
+                             None) == -1
+    assert L.medusa_heads_ex(*hx, 1, 0, 1, 64, 100, 1, 2, 1, None, p, None, p, 16, None) == -5
+    assert L.medusa_heads_ex_workspace(1, 64, 100, 1, 2, 1, 1) > L.medusa_heads_workspace(1, 64, 100, 1, 1)
+    assert L.medusa_heads_ex_workspace(1, 64, 100, 1, 1, 0, 1) == L.medusa_heads_workspace(1, 64, 100, 1, 1)
     assert L.medusa_stream_read(p, 24, p, None) == -2
     assert L.medusa_stream_read(p, 0, p, None) == -2
     assert L.medusa_stream_read(None, 32, p, None) == -1
