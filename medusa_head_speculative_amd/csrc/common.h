@@ -100,6 +100,27 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* scratch)
   return r;
 }
 
+// Combine a value with the one in lane i ^ 16 (i ^ 32) without LDS: v_permlane16_swap /
+// v_permlane32_swap with the value as both operands give, lane by lane, the own value and the
+// partner's (in one order or the other; the order was checked on the GPU and does not matter
+// for a max or a two-term sum).
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 16-byte global load of 8 bf16 as an MFMA operand
 __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
   uint4 v = *reinterpret_cast<const uint4*>(p);

@@ -299,8 +299,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sv[cb][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = xor32_max(xor16_max(mx));
       const float mxs = mx * a.sl2;
       if (mxs > mrow[mb] + 8.f) {                     // raise the reference (rare after the start)
         const float alpha = exp2f(mrow[mb] - mxs);
@@ -367,9 +366,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
   // ---- finish: full row sums, then the output or this split's partial ----
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    float l = lsum[mb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = xor32_sum(xor16_sum(lsum[mb]));
     const int m = qt * kAttnRows + wave * 32 + mb * 16 + mm;
     if (!rvalid[mb]) continue;
     if (a.splits == 1) {
