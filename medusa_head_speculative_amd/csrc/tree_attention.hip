@@ -215,7 +215,10 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
   }
 
   float mrow[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
+  // row sums of the (bf16) probabilities, accumulated on the matrix cores: P^T times a block of
+  // ones gives every lane the sum of its own query row in all four entries
+  f32x4_t lacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   f32x4_t oacc[2][NDB];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -304,7 +307,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
       if (mxs > mrow[mb] + 8.f) {                     // raise the reference (rare after the start)
         const float alpha = exp2f(mrow[mb] - mxs);
         mrow[mb] = mxs;
-        lsum[mb] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lacc[mb][j] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -319,7 +323,6 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
           // the hardware exp2 (v_exp_f32): results below 2^-126 flush to zero, which cannot
           // matter next to the row's largest term (>= 1 against the running reference)
           pr[cb][j] = __builtin_amdgcn_exp2f(fmaf(sv[cb][j], a.sl2, nm));
-          lsum[mb] += pr[cb][j];
         }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -351,6 +354,14 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
         }
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const uint4 bv = make_uint4(pb[mb][ks][0], pb[mb][ks][1], pb[mb][ks][2], pb[mb][ks][3]);
+        lacc[mb] = mfma16x16x32(ones, __builtin_bit_cast(bf16x8_t, bv), lacc[mb]);
+      }
+    }
     t = tn;
     buf ^= 1;
   };
@@ -366,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
   // ---- finish: full row sums, then the output or this split's partial ----
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    const float l = xor32_sum(xor16_sum(lsum[mb]));
+    const float l = lacc[mb][0];
     const int m = qt * kAttnRows + wave * 32 + mb * 16 + mm;
     if (!rvalid[mb]) continue;
     if (a.splits == 1) {
