@@ -26,6 +26,18 @@
  *                      evaluate_posterior(logits, candidates, temperature, posterior_threshold,
  *                      posterior_alpha, ...) -> (best_candidate, accept_length) and the
  *                      defaults 0.09 / 0.3.)
+ * Around the step:
+ *   5. commit_accepted      emits the accepted tokens, moves their K/V rows into place in the
+ *                           cache and hands over the next root and hidden state (Wiblog page,
+ *                           inference-flow section).
+ *   tree_attention_rope     tree_attention after the rotary embedding of the tree tokens at
+ *                           their depth positions (Wiblog page, tree-attention section).
+ *   medusa_sparse_tree      the N-node tree of largest expected accept length for given
+ *                           per-head rank accuracies (Ultralytics page, tree-attention section).
+ *   medusa_heads_ex         heads of several residual blocks, optionally opened by LayerNorm
+ *                           (Wiblog page, heads section).
+ * For measurement only: medusa_set_kernel_events (HIP events around each kernel family) and
+ * medusa_stream_read (a plain HBM read, the bandwidth ceiling the heads are compared with).
  *
  * Conventions for every entry point:
  *   - Pointers marked "device" are HIP device memory on the current device; "host" pointers are
