@@ -56,28 +56,33 @@ __device__ __forceinline__ s16x4_t lds_read_tr(const uint16_t* p) {
 }
 
 // LDS tile layout: 64 K (or V) rows of D bf16, rows back to back; the 16-byte chunks of a row are
-// permuted by an XOR with a row-dependent slot key, so that both operand reads below are free of
-// bank conflicts: the K reads (16 rows, one chunk) and the transposed V reads (4 consecutive rows,
-// 2 chunks).  The direct global->LDS loads write 64 consecutive 16-byte slots per wave
-// instruction, so the permutation is applied on the global side: the lane that fills slot s of
-// row r loads chunk s ^ key(r).
+// permuted by an XOR with a row-dependent slot key.  The direct global->LDS loads write 64
+// consecutive 16-byte slots per wave instruction, so the permutation is applied on the global
+// side: the lane that fills slot s of row r loads chunk s ^ key(r).
+// For D = 128 the key is 2 * (r mod 8).  With it the bank-conflict counter reads zero for both
+// operand reads below, which then run at the rate of linear reads: 4 LDS cycles per 16-byte K read
+// (16 rows, one chunk each; the earlier key cost 8) and 2 per transposed V read (8 rows of a
+// half-wave, 2 chunks each; the earlier key cost 4).  The transposed reads see 64 four-byte banks
+// per half-wave, so the 8 rows of a half-wave must use 8 different chunk pairs; the 16-byte reads
+// group lanes in a way that rows 0-7 against rows 8-15 of one chunk do not disturb.
 template <int D>
 __device__ __forceinline__ int slot_key(int r) {
   if constexpr (D == 128) {
-    const int q = r & 15;
-    return ((q & 3) << 1) | ((q >> 2) & 1) | (q & 8);
+    return (r & 7) << 1;
   } else {
     return (r >> 1) & 7;
   }
 }
+
 template <int D>
 __device__ __forceinline__ int tile_elem(int r, int c) {   // element offset of (row r, chunk c)
   return r * D + ((c ^ slot_key<D>(r)) << 3);
 }
 
 // The operand reads below touch rows whose slot key depends on the lane only (the row bits that
-// vary from read to read are above bit 3 for D = 128, above bit 4 for D = 64), so every address
-// is one per-lane base XOR a compile-time block index: no per-read address registers.
+// vary from read to read are above bit 3; the key reads bits 0-2 for D = 128, 1-3 for D = 64),
+// so every address is one per-lane base XOR a compile-time block index: no per-read address
+// registers.
 //   K fragment (cb, kb): row cb*16 + mm, chunk kb*4 + lg  ->  (kbase ^ (kb << 5)) + cb*16*D
 //   V fragment (db, ks, hi): row ks*32 + hi*16 + 4*lg + mm/4, chunk db*2 + (mm&3)/2, +4 if mm odd
 //                        ->  (vbase ^ (db << 4)) + (ks*32 + hi*16)*D
