@@ -28,7 +28,9 @@ def run_attn(m, a, mask, Hkv, max_pl=None):
 
 def _sample_units(B, Hq, T, n, seed):
     rng = rng_for(seed, 9)
-    sel = [(0, h, i) for h in range(Hq) for i in {0, 1, T // 2, T - 1}]
+    # every head of the first and the last sequence at a few nodes (the last sequence's units are
+    # the ones the work plan runs last, cut into K/V splits), plus random rows
+    sel = [(b, h, i) for b in {0, B - 1} for h in range(Hq) for i in {0, 1, T // 2, T - 1}]
     sel += [(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(T))) for _ in range(n)]
     return np.array(sorted(set(sel)), np.int32)
 
