@@ -290,7 +290,19 @@ def main():
     torch.cuda.synchronize()
     ceiling_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in cev]))
     ceiling_gbs = CEILING_BYTES / (ceiling_ms * 1e-3) / 1e9
-    del buf, sink
+    # the same plain read over exactly the vocab projection's weight bytes: a ceiling for one
+    # launch of that size, start-up and drain included
+    w2_weight_bytes = (cfg.K * cfg.V * cfg.Hd * cfg.esize) // 16 * 16
+    same = buf[:w2_weight_bytes] if w2_weight_bytes <= CEILING_BYTES else None
+    same_ms = None
+    if same is not None:
+        for e0, e1 in cev:
+            e0.record(stream)
+            m.stream_read(same, sink)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        same_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in cev]))
+    del buf, sink, same
     for ent in kernels.values():
         if "GB/s" in ent:
             ent["ceiling_frac"] = round(ent["GB/s"] / ceiling_gbs, 4)
@@ -371,7 +383,9 @@ def main():
                           if cfg.dtype == "bf16" else "heads_gemv_f32 (vocab projection W2)",
                 "alg_bytes_per_launch": w2_bytes, "avg_launch_ms": round(w2_ms, 5),
                 "measured_read_ceiling_GB/s": round(ceiling_gbs, 1),
-                "frac_of_measured_ceiling": round(achieved / ceiling_gbs, 4)}
+                "frac_of_measured_ceiling": round(achieved / ceiling_gbs, 4),
+                "plain_read_same_weight_bytes_ms": None if same_ms is None else round(same_ms, 5),
+                "frac_of_plain_read_same_bytes": None if same_ms is None else round(same_ms / w2_ms, 4)}
 
     if args.copy_calibration:
         src = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")   # 256 MiB
