@@ -35,10 +35,11 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// 64-bit selection key: larger value wins, equal values -> lower index wins.  Key 0 is below
-// every real key (a real key has a float_key >= 0x007fffff in its high word).
+// 64-bit selection key: larger value wins, equal values -> lower index wins.  -0 is keyed as +0
+// (v + 0 turns -0 into +0), so the two zeros count as equal, as in a numeric comparison.  Key 0
+// is below every real key (a real key has a float_key >= 0x007fffff in its high word).
 __device__ __forceinline__ uint64_t sel_key(float v, uint32_t idx) {
-  return (static_cast<uint64_t>(float_key(v)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
+  return (static_cast<uint64_t>(float_key(v + 0.0f)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
 }
 __device__ __forceinline__ uint32_t sel_key_index(uint64_t k) {
   return 0xffffffffu - static_cast<uint32_t>(k & 0xffffffffu);

@@ -181,37 +181,68 @@ __global__ __launch_bounds__(kAccThreads) void accept_chunks(AcceptArgs a) {
 #pragma unroll
   for (int u = 0; u < U; ++u) load8(row, a.dtype, base + u * kAccVec, a.V, x[u], valid[u]);
   uint64_t arg = 0;
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int e = 0; e < kAccPerThread; ++e)
-      if (valid[u][e]) {
-        const uint64_t k = sel_key(x[u][e], static_cast<uint32_t>(base + u * kAccVec + e));
-        arg = k > arg ? k : arg;
-      }
   RowStat st{-INFINITY, 0.f, 0.f, 0.f};
-  if (!a.greedy) {
-    float m = -INFINITY;
+  if ((c + 1) * static_cast<long>(kAccVec) * U <= a.V) {
+    // every element of the chunk is in the row (all chunks but a ragged last one): the argmax as
+    // a float compare in index order (the first maximum wins; -0 == +0), the row statistics from
+    // its value, with the hardware exp2.  A -inf logit contributes nothing: its exponent is
+    // clamped to -256, where v_exp_f32 returns 0.
+    float best = -INFINITY;
+    int bpos = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int e = 0; e < kAccPerThread; ++e)
-        if (valid[u][e]) m = fmaxf(m, x[u][e] * a.y_scale);
-    if (m > -INFINITY) {
+        if (x[u][e] > best) {
+          best = x[u][e];
+          bpos = u * kAccPerThread + e;
+        }
+    // (a thread whose elements are all -inf keeps its first one, like any tie)
+    arg = sel_key(best, static_cast<uint32_t>(base + (bpos / kAccPerThread) * kAccVec + bpos % kAccPerThread));
+    if (!a.greedy && best > -INFINITY) {
+      const float m = best * a.y_scale;
       float S = 0.f, A = 0.f;
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < kAccPerThread; ++e) {
-          if (!valid[u][e]) continue;
-          const float d = x[u][e] * a.y_scale - m;
-          const float p = exp2f(d);
-          if (p > 0.f) {
-            S += p;
-            A += d * p;
-          }
+          const float d = fmaxf(fmaf(x[u][e], a.y_scale, -m), -256.f);
+          const float p = __builtin_amdgcn_exp2f(d);
+          S += p;
+          A = fmaf(d, p, A);
         }
       st = RowStat{m, S, A, 0.f};
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < kAccPerThread; ++e)
+        if (valid[u][e]) {
+          const uint64_t k = sel_key(x[u][e], static_cast<uint32_t>(base + u * kAccVec + e));
+          arg = k > arg ? k : arg;
+        }
+    if (!a.greedy) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < kAccPerThread; ++e)
+          if (valid[u][e]) m = fmaxf(m, x[u][e] * a.y_scale);
+      if (m > -INFINITY) {
+        float S = 0.f, A = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int e = 0; e < kAccPerThread; ++e) {
+            if (!valid[u][e]) continue;
+            const float d = fmaxf(fmaf(x[u][e], a.y_scale, -m), -256.f);
+            const float p = __builtin_amdgcn_exp2f(d);
+            S += p;
+            A = fmaf(d, p, A);
+          }
+        st = RowStat{m, S, A, 0.f};
+      }
     }
   }
   block_merge(st, arg, a.greedy, s_stat, s_arg);

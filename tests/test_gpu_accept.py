@@ -115,6 +115,28 @@ def test_accept_uniform_rows_accept_everything_and_neg_inf_rows():
     assert (best[1], alen[1], nxt[1]) == (res["best_candidate"][1], res["accept_length"][1], 17)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_accept_signed_zero_maxima_tie(dtype):
+    """A row whose maximum is 0, held as -0 at index 2, +0 at 6 and -0 at 9 (2 and 6 in one
+    thread's eight elements, 9 in the next): the zeros compare equal, so the argmax is the
+    first of them, 2, as the oracle's numeric argmax has it.  Greedy: no candidate token is 2,
+    so nothing is accepted and the next token is the root row's argmax."""
+    m = lib()
+    choices = load_tree_choices("c1")
+    V, B = 3000, 1
+    st, tr, tokens = _tree_and_tokens(m, choices, 4, 10, B, V, seed=2)
+    tokens = np.where(tokens == 2, 3, tokens).astype(np.int32)
+    f = np.full((B, st["T"], V), -1.0, np.float32)
+    f[:, :, [2, 9]] = -0.0
+    f[:, :, 6] = 0.0
+    logits = f if dtype == "f32" else (f.view(np.uint32) >> 16).astype(np.uint16)
+    say("accept signed zeros", dtype)
+    best, alen, nxt = run_accept(m, tr, logits, tokens, 0.0)
+    res = oracle.typical_accept(logits, dtype, tokens, st, 0.0)
+    assert res["accept_length"][0] == 0 and res["next_token"][0] == 2
+    assert (int(alen[0]), int(nxt[0])) == (0, 2)
+
+
 def test_accept_strict_parameters_and_determinism():
     m = lib()
     cfg = get_config(1)
