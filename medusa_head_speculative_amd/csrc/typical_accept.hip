@@ -254,26 +254,47 @@ __global__ __launch_bounds__(kAccThreads) void accept_chunks(AcceptArgs a) {
 }
 
 // argmax (lowest index on ties) of one row by a block of NT threads, UR rounds of 8 elements
-// per thread in flight
+// per thread in flight.  Each thread keeps its best value and index with float compares in
+// increasing index order (the first maximum wins; -0 == +0) and keys them once at the end; a
+// thread with no element of the row contributes key 0.
 template <int NT, int UR>
 __device__ __forceinline__ uint64_t block_row_argmax(const void* row, int dtype, long V,
                                                      uint64_t* scratch) {
   constexpr long kStep = static_cast<long>(NT) * kAccPerThread;
-  uint64_t arg = 0;
+  float best = -INFINITY;
+  long bidx = -1;
   for (long j0 = static_cast<long>(threadIdx.x) * kAccPerThread; j0 < V; j0 += UR * kStep) {
     float x[UR][kAccPerThread];
     bool valid[UR][kAccPerThread];
 #pragma unroll
     for (int u = 0; u < UR; ++u) load8(row, dtype, j0 + u * kStep, V, x[u], valid[u]);
+    if (bidx < 0) {                                   // this thread's first element (j0 < V)
+      best = x[0][0];
+      bidx = j0;
+    }
+    int bpos = -1;                                    // best position in this sweep, if any
+    if (j0 + (UR - 1) * kStep + kAccPerThread <= V) {
 #pragma unroll
-    for (int u = 0; u < UR; ++u)
+      for (int u = 0; u < UR; ++u)
 #pragma unroll
-      for (int e = 0; e < kAccPerThread; ++e)
-        if (valid[u][e]) {
-          const uint64_t k = sel_key(x[u][e], static_cast<uint32_t>(j0 + u * kStep + e));
-          arg = k > arg ? k : arg;
-        }
+        for (int e = 0; e < kAccPerThread; ++e)
+          if (x[u][e] > best) {
+            best = x[u][e];
+            bpos = u * kAccPerThread + e;
+          }
+    } else {
+#pragma unroll
+      for (int u = 0; u < UR; ++u)
+#pragma unroll
+        for (int e = 0; e < kAccPerThread; ++e)
+          if (valid[u][e] && x[u][e] > best) {
+            best = x[u][e];
+            bpos = u * kAccPerThread + e;
+          }
+    }
+    if (bpos >= 0) bidx = j0 + (bpos / kAccPerThread) * kStep + bpos % kAccPerThread;
   }
+  const uint64_t arg = bidx < 0 ? 0ull : sel_key(best, static_cast<uint32_t>(bidx));
   return block_max_u64<NT>(arg, scratch);
 }
 
