@@ -8,9 +8,14 @@
 // when they were written; this kernel rotates the tree tokens' queries (into a buffer) and their
 // key rows in the cache (in place), rounding to the storage type (nearest even for bf16).
 //
-// One wave per row (query row or cache key row), lane i < D/2 owns the pair (i, i + D/2).  The
-// angle is formed and reduced to [-pi, pi] in fp64 (at position 8192 an fp32 angle would already
-// be off by ~5e-4 rad), then sin/cos and the rotation run in fp32.
+// The rows of one tree node share their angles, so a work-group takes one (sequence, node) and a
+// chunk of up to 32 of its rows (q heads, then kv heads), 8 per wave.  A lane owns 4 consecutive
+// pairs (i, i + D/2) of one row, so a wave instruction covers 64 / (D/8) rows with 8-byte (bf16)
+// or 16-byte (fp32) accesses.  Every wave issues its rows' loads first; meanwhile wave 0 forms
+// the node's D/2 angles and their cos/sin into LDS.  An angle is formed and reduced to [-pi, pi]
+// in fp64 (at position 8192 an fp32 angle would already be off by ~5e-4 rad), from inverse
+// frequencies base^(-2i/D) computed once on the host in fp64; sin/cos and the rotation run in
+// fp32.
 #include <math.h>
 
 #include "common.h"
@@ -19,71 +24,117 @@
 namespace medusa {
 
 constexpr int kRopeThreads = 256;
-constexpr unsigned kRopeMaxGrid = 2048;
+constexpr int kRopeRowsPerWg = 32;            // 8 rows per wave
+constexpr unsigned kRopeMaxGrid = 65535;
 
+struct RopeKArgs {
+  RopeArgs a;
+  double inv[64];                             // base^(-2i/D), i < D/2
+};
+
+// 4 consecutive elements at element offset i (a multiple of 4)
 template <bool BF16>
-__device__ __forceinline__ float rope_load(const void* p, long i) {
-  return BF16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+__device__ __forceinline__ float4 rope_load4(const void* p, long i) {
+  if (BF16) {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    return make_float4(bf16_to_f32(static_cast<uint16_t>(v.x)), bf16_to_f32(static_cast<uint16_t>(v.x >> 16)),
+                       bf16_to_f32(static_cast<uint16_t>(v.y)), bf16_to_f32(static_cast<uint16_t>(v.y >> 16)));
+  }
+  return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
 }
 template <bool BF16>
-__device__ __forceinline__ void rope_store(void* p, long i, float v) {
-  if (BF16) static_cast<uint16_t*>(p)[i] = f32_to_bf16_rne(v);
-  else static_cast<float*>(p)[i] = v;
+__device__ __forceinline__ void rope_store4(void* p, long i, float4 v) {
+  if (BF16) {
+    uint2 w;
+    w.x = static_cast<uint32_t>(f32_to_bf16_rne(v.x)) | (static_cast<uint32_t>(f32_to_bf16_rne(v.y)) << 16);
+    w.y = static_cast<uint32_t>(f32_to_bf16_rne(v.z)) | (static_cast<uint32_t>(f32_to_bf16_rne(v.w)) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = w;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = v;
+  }
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kRopeThreads) void rope_tree_kernel(RopeArgs a) {
-  __shared__ double s_inv[64];
+__global__ __launch_bounds__(kRopeThreads) void rope_tree_kernel(RopeKArgs k) {
+  const RopeArgs& a = k.a;
+  __shared__ __align__(16) float s_cs[64];
+  __shared__ __align__(16) float s_sn[64];
   const int half = a.D / 2;
-  for (int i = threadIdx.x; i < half; i += kRopeThreads)
-    s_inv[i] = pow(static_cast<double>(a.base), -2.0 * i / a.D);
-  __syncthreads();
+  const int lpr = half / 4;                                  // lanes per row
+  const int rpi = 64 / lpr;                                  // rows per wave instruction
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const long qrows = static_cast<long>(a.B) * a.Hq * a.T;
-  const long rows = qrows + static_cast<long>(a.B) * a.Hkv * a.T;
+  const int q4 = (lane % lpr) * 4;                           // this lane's first pair index
+  const int R = a.Hq + a.Hkv;                                // rows of one node
+  const int chunks = (R + kRopeRowsPerWg - 1) / kRopeRowsPerWg;
+  const long items = static_cast<long>(a.B) * a.T * chunks;
   const double two_pi = 6.283185307179586476925286766559;
   const double inv_two_pi = 0.15915494309189533576888376337251;
-  for (long r = static_cast<long>(blockIdx.x) * 4 + wave; r < rows; r += static_cast<long>(gridDim.x) * 4) {
-    const void* src;
-    void* dst;
-    long base;
-    int b, n;
-    if (r < qrows) {
-      b = static_cast<int>(r / (static_cast<long>(a.Hq) * a.T));
-      n = static_cast<int>(r % a.T);
-      src = a.q;
-      dst = a.q_rot;
-      base = r * a.D;
-    } else {
-      const long r2 = r - qrows;
-      b = static_cast<int>(r2 / (static_cast<long>(a.Hkv) * a.T));
-      const int g = static_cast<int>((r2 / a.T) % a.Hkv);
-      n = static_cast<int>(r2 % a.T);
-      const int L = min(max(a.prefix_len[b], 0), a.Lmax);   // as tree attention reads it
-      src = a.kc;
-      dst = a.kc;
-      base = ((static_cast<long>(b) * a.Hkv + g) * a.lcap + L + n) * a.D;
+  for (long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int ch = static_cast<int>(it % chunks);
+    const long bn = it / chunks;
+    const int b = static_cast<int>(bn / a.T), n = static_cast<int>(bn % a.T);
+    const int L = min(max(a.prefix_len[b], 0), a.Lmax);    // as tree attention reads it
+    // this wave's 8 rows: rows ch*32 + wave*8 + g*rpi + lane/lpr, g < 8/rpi
+    constexpr int kMaxG = 2;                               // 8 rows / rpi: 2 for D = 128, 1 for D = 64
+    float4 x[kMaxG], y[kMaxG];
+    long base[kMaxG];
+    void* dst[kMaxG];
+#pragma unroll
+    for (int g = 0; g < kMaxG; ++g) {
+      base[g] = -1;
+      const int j = ch * kRopeRowsPerWg + wave * 8 + g * rpi + lane / lpr;
+      if (g * rpi < 8 && j < R) {
+        const void* src;
+        if (j < a.Hq) {
+          src = a.q;
+          dst[g] = a.q_rot;
+          base[g] = ((static_cast<long>(b) * a.Hq + j) * a.T + n) * a.D;
+        } else {
+          src = a.kc;
+          dst[g] = a.kc;
+          base[g] = ((static_cast<long>(b) * a.Hkv + (j - a.Hq)) * a.lcap + L + n) * a.D;
+        }
+        x[g] = rope_load4<BF16>(src, base[g] + q4);
+        y[g] = rope_load4<BF16>(src, base[g] + q4 + half);
+      }
     }
-    if (lane < half) {
-      const double ang = static_cast<double>(a.pos[static_cast<long>(b) * a.T + n]) * s_inv[lane];
+    __syncthreads();                                        // the last item's readers are done
+    if (wave == 0 && lane < half) {
+      const double ang = static_cast<double>(a.pos[bn]) * k.inv[lane];
       const float red = static_cast<float>(fma(-two_pi, rint(ang * inv_two_pi), ang));
       float sn, cs;
       sincosf(red, &sn, &cs);
-      const float x = rope_load<BF16>(src, base + lane);
-      const float y = rope_load<BF16>(src, base + lane + half);
-      rope_store<BF16>(dst, base + lane, fmaf(x, cs, -(y * sn)));
-      rope_store<BF16>(dst, base + lane + half, fmaf(x, sn, y * cs));
+      s_cs[lane] = cs;
+      s_sn[lane] = sn;
+    }
+    __syncthreads();
+    const float4 cs = *reinterpret_cast<const float4*>(s_cs + q4);
+    const float4 sn = *reinterpret_cast<const float4*>(s_sn + q4);
+#pragma unroll
+    for (int g = 0; g < kMaxG; ++g) {
+      if (base[g] < 0) continue;
+      const float4 xv = x[g], yv = y[g];
+      rope_store4<BF16>(dst[g], base[g] + q4,
+                        make_float4(fmaf(xv.x, cs.x, -(yv.x * sn.x)), fmaf(xv.y, cs.y, -(yv.y * sn.y)),
+                                    fmaf(xv.z, cs.z, -(yv.z * sn.z)), fmaf(xv.w, cs.w, -(yv.w * sn.w))));
+      rope_store4<BF16>(dst[g], base[g] + q4 + half,
+                        make_float4(fmaf(xv.x, sn.x, yv.x * cs.x), fmaf(xv.y, sn.y, yv.y * cs.y),
+                                    fmaf(xv.z, sn.z, yv.z * cs.z), fmaf(xv.w, sn.w, yv.w * cs.w)));
     }
   }
 }
 
 hipError_t launch_rope_tree(const RopeArgs& a, int dtype, hipStream_t s) {
-  const long rows = static_cast<long>(a.B) * (a.Hq + a.Hkv) * a.T;
-  long blocks = (rows + 3) / 4;
-  const unsigned grid = static_cast<unsigned>(blocks < kRopeMaxGrid ? blocks : kRopeMaxGrid);
+  RopeKArgs k{};
+  k.a = a;
+  for (int i = 0; i < a.D / 2 && i < 64; ++i)
+    k.inv[i] = pow(static_cast<double>(a.base), -2.0 * i / a.D);
+  const int R = a.Hq + a.Hkv;
+  const long items = static_cast<long>(a.B) * a.T * ((R + kRopeRowsPerWg - 1) / kRopeRowsPerWg);
+  const unsigned grid = static_cast<unsigned>(items < kRopeMaxGrid ? items : kRopeMaxGrid);
   hook_before(K_ROPE, s);
-  if (dtype == 1) rope_tree_kernel<true><<<grid, kRopeThreads, 0, s>>>(a);
-  else rope_tree_kernel<false><<<grid, kRopeThreads, 0, s>>>(a);
+  if (dtype == 1) rope_tree_kernel<true><<<grid, kRopeThreads, 0, s>>>(k);
+  else rope_tree_kernel<false><<<grid, kRopeThreads, 0, s>>>(k);
   hook_after(K_ROPE, s);
   return hipGetLastError();
 }
