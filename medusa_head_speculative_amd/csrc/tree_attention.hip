@@ -525,10 +525,27 @@ __global__ __launch_bounds__(64) void tree_attn_f32(const float* __restrict__ q,
     __syncthreads();
     o0 *= alpha;
     o1 *= alpha;
+    // p-weighted V rows, 8 rows' loads in flight before their FMAs (same order of summation;
+    // an invisible column has p = 0 and a finite V row, so it adds nothing)
     const int nc = static_cast<int>(min(static_cast<long>(64), ncols - c0));
-    for (int cc = 0; cc < nc; ++cc) {
+    int cc = 0;
+    for (; cc + 8 <= nc; cc += 8) {
+      float v0[8], v1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* vr = vc + (base + c0 + cc + u) * D;
+        v0[u] = lane < D ? vr[lane] : 0.f;
+        v1[u] = lane + 64 < D ? vr[lane + 64] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float pc = s_p[cc + u];
+        o0 = fmaf(pc, v0[u], o0);
+        o1 = fmaf(pc, v1[u], o1);
+      }
+    }
+    for (; cc < nc; ++cc) {
       const float pc = s_p[cc];
-      if (pc == 0.f) continue;
       const float* vr = vc + (base + c0 + cc) * D;
       if (lane < D) o0 = fmaf(pc, vr[lane], o0);
       if (lane + 64 < D) o1 = fmaf(pc, vr[lane + 64], o1);
