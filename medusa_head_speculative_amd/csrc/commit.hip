@@ -9,8 +9,9 @@
 // sequence in order; the prefix grows by a + 1; next_token becomes the next root, and the last
 // accepted node's hidden state is what the next step's heads read.
 //
-// One work-group per sequence.  A thread owns some (kv head, K or V, 16-byte column) slots and
-// walks them in increasing depth: node ids grow with depth (path[k] >= k), so no destination
+// One work-group of 1024 threads per sequence (one work-group, so the in-place update of
+// prefix_len stays safe).  A thread owns some (kv head, K or V, 16-byte column) slots and walks
+// them in increasing depth: node ids grow with depth (path[k] >= k), so no destination
 // row L + k is the source of a later depth, and each store depends on the load just before it,
 // which orders every read of a row before any later write to it.
 #include "common.h"
@@ -18,7 +19,7 @@
 
 namespace medusa {
 
-constexpr int kCommitThreads = 256;
+constexpr int kCommitThreads = 1024;
 
 __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitArgs a) {
   const int b = blockIdx.x;
