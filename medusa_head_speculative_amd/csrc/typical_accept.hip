@@ -359,32 +359,70 @@ __global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
 template <int NT>
 __global__ __launch_bounds__(NT) void accept_paths(AcceptArgs a) {
   constexpr int kPathThreads = NT;
+  constexpr int kPathRegs = 8;                        // path nodes held in registers
   __shared__ uint64_t s_scratch[kPathThreads / 64];
   __shared__ int32_t s_dec[kMaxTreeTokens];
+  __shared__ uint8_t s_leaf[kMaxTreeTokens];
+  __shared__ int32_t s_last;
   const int b = blockIdx.x;
-  if (threadIdx.x == 0) s_dec[0] = 1;
-  for (int i = 1 + threadIdx.x; i < a.T; i += kPathThreads) s_dec[i] = a.dec[static_cast<long>(b) * a.T + i];
+  // every static load goes out before anything waits: this thread's path (nodes after the root,
+  // the first kPathRegs of them; trees are at most 8 deep) and length, the decisions, and which
+  // nodes are leaves
+  int pn[kPathRegs];
+  int plen = 0, loaded = -1;
+  auto load_path = [&](int p) {
+    const int32_t* path = a.paths + static_cast<long>(p) * (a.dmax + 1);
+    plen = a.path_len[p];
+#pragma unroll
+    for (int j = 0; j < kPathRegs; ++j) pn[j] = path[min(j + 1, a.dmax)];
+    loaded = p;
+  };
+  if (static_cast<int>(threadIdx.x) < a.n_paths) load_path(threadIdx.x);
+  for (int i = threadIdx.x; i < a.T; i += kPathThreads) {
+    s_dec[i] = i == 0 ? 1 : a.dec[static_cast<long>(b) * a.T + i];
+    s_leaf[i] = a.child_ptr[i + 1] == a.child_ptr[i];
+  }
   __syncthreads();
   uint64_t bestk = 0;
   for (int p = threadIdx.x; p < a.n_paths; p += kPathThreads) {
-    const int32_t* path = a.paths + static_cast<long>(p) * (a.dmax + 1);
-    const int len = a.path_len[p];
+    if (p != loaded) load_path(p);
     int k = 0;
-    while (k < len && s_dec[path[k + 1]]) ++k;
+    bool go = true;
+#pragma unroll
+    for (int j = 0; j < kPathRegs; ++j) {
+      if (go && j < plen && s_dec[pn[j]]) ++k;
+      else go = false;
+    }
+    if (go && plen > kPathRegs) {                     // deeper than the registers hold
+      const int32_t* path = a.paths + static_cast<long>(p) * (a.dmax + 1);
+      while (k < plen && s_dec[path[k + 1]]) ++k;
+    }
     const uint64_t key = (static_cast<uint64_t>(k) << 32) | (0xffffffffu - static_cast<uint32_t>(p));
     bestk = key > bestk ? key : bestk;
   }
   bestk = block_max_u64<kPathThreads>(bestk, s_scratch);
   const int p = static_cast<int>(0xffffffffu - static_cast<uint32_t>(bestk & 0xffffffffu));
   const int k = static_cast<int>(bestk >> 32);
-  const int last = a.paths[static_cast<long>(p) * (a.dmax + 1) + k];
-  if (threadIdx.x == 0) {
+  if (static_cast<int>(threadIdx.x) == p % kPathThreads) {   // the thread that walked path p
+    int last = 0;                                            // the root when nothing is accepted
+    if (k > 0) {
+      if (loaded == p && k <= kPathRegs) {
+#pragma unroll
+        for (int j = 0; j < kPathRegs; ++j)
+          if (j == k - 1) last = pn[j];
+      } else {
+        last = a.paths[static_cast<long>(p) * (a.dmax + 1) + k];
+      }
+    }
+    s_last = last;
     a.best[b] = p;
     a.accept_len[b] = k;
   }
   if (!a.next_token) return;
+  __syncthreads();
+  const int last = s_last;
   // the greedy token after the last accepted node; its argmax is known if it has children
-  if (a.child_ptr[last + 1] > a.child_ptr[last]) {
+  if (!s_leaf[last]) {
     if (threadIdx.x == 0) a.next_token[b] = a.rowarg[static_cast<long>(b) * a.T + last];
   } else {
     const int esz = a.dtype == 1 ? 2 : 4;
