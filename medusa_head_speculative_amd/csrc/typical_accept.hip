@@ -32,16 +32,14 @@ constexpr int kAccPerThread = 8;
 constexpr int kAccVec = kAccThreads * kAccPerThread;    // elements per load round of a work-group
 constexpr long kPathWideBytes = 32 << 10;   // leaf rows above this size get a 1024-thread block
 constexpr int kMaxTreeTokens = 4096;
-constexpr long kAccTargetGroups = 1024;
-
-// Load rounds per chunk: the largest of 8, 4, 2 whose chunk count still gives at least
-// kAccTargetGroups work-groups, else 1 (small problems stay spread over many CUs).
+constexpr long kAccTargetGroups = 2048;
+// Rounds of kAccVec elements per work-group of accept_chunks: 2 when that still leaves at least
+// kAccTargetGroups work-groups, else 1 (small problems stay spread over many CUs).  Measured on
+// MI355X: the 70B-layer rows took 68 us at 2 rounds against 70 at 4 and 75 at 8; the 33B rows
+// 34 us at 2 or 4; the 7B rows (512 work-groups) 14.6 us at 1 against 15.7 at 2.
 static int accept_unroll(int B, long V, int n_int) {
-  for (int u = 8; u > 1; u >>= 1) {
-    const long C = (V + static_cast<long>(kAccVec) * u - 1) / (static_cast<long>(kAccVec) * u);
-    if (C * n_int * B >= kAccTargetGroups) return u;
-  }
-  return 1;
+  const long C = (V + static_cast<long>(kAccVec) * 2 - 1) / (static_cast<long>(kAccVec) * 2);
+  return C * n_int * B >= kAccTargetGroups ? 2 : 1;
 }
 
 struct RowStat {   // partial softmax statistics of a set of elements (log2 units)
@@ -485,8 +483,6 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, lo
   const dim3 grid(L.chunks, n_internal, B);
   hook_before(K_ACCEPT, s);
   switch (L.unroll) {
-    case 8: accept_chunks<8><<<grid, kAccThreads, 0, s>>>(a); break;
-    case 4: accept_chunks<4><<<grid, kAccThreads, 0, s>>>(a); break;
     case 2: accept_chunks<2><<<grid, kAccThreads, 0, s>>>(a); break;
     default: accept_chunks<1><<<grid, kAccThreads, 0, s>>>(a); break;
   }
