@@ -13,8 +13,8 @@
 // handoff is a kernel boundary):
 //   accept_chunks  one work-group per (sequence, internal row, chunk) computes in a single pass
 //                  the chunk's max y, S = sum 2^(y - max) and A = sum (y - max) 2^(y - max) with
-//                  y = l * log2(e) / T, plus the argmax (a chunk is 1-8 rounds of 8 elements per
-//                  thread, the most that still leaves about a thousand work-groups);
+//                  y = l * log2(e) / T, plus the argmax (a chunk is 1 or 2 rounds of 8 elements
+//                  per thread, see accept_unroll);
 //   accept_rows    one work-group per (sequence, internal row) merges the row's partials in chunk
 //                  order, so H = ln2 * (log2 S - A / S) and ln p(x) = ln2 * (y_x - max - log2 S),
 //                  and decides the row's children in the log domain;
