@@ -252,7 +252,7 @@ size_t tree_attention_workspace(int B, int Hq, int Hkv, int T, int D, int max_pr
  * Arithmetic: fp32 scores, softmax and accumulation; bf16 operands enter the matrix cores
  * directly; the output is rounded to dtype (nearest even).
  * Limits: D in {64, 128}, Hq % Hkv == 0, 1 <= T <= 4096, 0 <= max_prefix_len <= 1<<20,
- *         1 <= B, Hq <= 256.
+ *         1 <= B <= 4096, Hq <= 256.
  */
 int tree_attention(const void* q, const void* k_cache, const void* v_cache, int dtype,
                    const int32_t* prefix_len, int max_prefix_len, long lcap,

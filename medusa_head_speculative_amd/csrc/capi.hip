@@ -298,8 +298,8 @@ int build_tree(const int32_t* choices, int n_choices, int max_depth, int K, int 
 
 // ---- tree attention -------------------------------------------------------------------------
 static int attn_shape(int B, int Hq, int Hkv, int T, int D, int max_prefix_len) {
-  if (B < 1 || Hq < 1 || Hq > 256 || Hkv < 1 || Hq % Hkv)
-    return fail(MEDUSA_ERR_SHAPE, "B = %d, Hq = %d, Hkv = %d (need Hq %% Hkv == 0, Hq <= 256)", B, Hq, Hkv);
+  if (B < 1 || B > 4096 || Hq < 1 || Hq > 256 || Hkv < 1 || Hq % Hkv)
+    return fail(MEDUSA_ERR_SHAPE, "B = %d, Hq = %d, Hkv = %d (need B <= 4096, Hq %% Hkv == 0, Hq <= 256)", B, Hq, Hkv);
   if (D != 64 && D != 128) return fail(MEDUSA_ERR_SHAPE, "D = %d, need 64 or 128", D);
   if (T < 1 || T > 4096) return fail(MEDUSA_ERR_SHAPE, "T = %d, need 1..4096", T);
   if (max_prefix_len < 0 || max_prefix_len > (1 << 20)) return fail(MEDUSA_ERR_SHAPE, "max_prefix_len = %d", max_prefix_len);

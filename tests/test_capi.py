@@ -86,6 +86,7 @@ def test_workspace_queries(m):
     assert m.tree_attention_workspace(1, 32, 32, 65, 128, 1024) > 0
     assert m.tree_attention_workspace(1, 32, 5, 65, 128, 1024) == 0  # Hq % Hkv
     assert m.tree_attention_workspace(1, 32, 32, 65, 96, 1024) == 0  # D
+    assert m.tree_attention_workspace(4097, 32, 32, 65, 128, 1024) == 0  # B
     assert m.typical_accept_workspace(1, 65, 32000, 32) > 0
     assert m.typical_accept_workspace(1, 65, 32000, 65) == 0
 
