@@ -226,22 +226,28 @@ def main():
     del kc_commit, vc_commit
     for k in names:
         m.set_kernel_events(k, None, None)
-    # the rotary-embedding variant of tree attention: its rotation kernel alone, on a copy of the
-    # cache (it rotates the tree key rows in place), with only its own hook set
+    # the rotary-embedding variant of tree attention, on a copy of the cache (it rotates the tree
+    # key rows in place): its key-rotation kernel ("rope") and its attention kernel, which
+    # rotates the queries as it loads them ("attention_rope")
     kc_rope = kc.clone()
     out_rope = torch.empty_like(out)
     ws_rope = m.workspace(m.tree_attention_rope_workspace(cfg.B, cfg.Hq, cfg.Hkv, T, cfg.D, cfg.L))
     events["rope"] = make_events(nb)
+    events["attention_rope"] = make_events(nb)
     for i in range(nb):
         m.set_kernel_events("rope", *events["rope"][i])
+        m.set_kernel_events("attention", *events["attention_rope"][i])
         m.tree_attention_rope(q, kc_rope, vc, pl, cfg.L, step.tree.mask, step.position_ids,
                               out_rope, ws_rope)
     torch.cuda.synchronize()
     m.set_kernel_events("rope", None, None)
+    m.set_kernel_events("attention", None, None)
     del kc_rope, out_rope, ws_rope
     kb = kernel_bytes(cfg, T, n_int)
-    # rope: every tree query row and tree key row read and written once
-    kb["rope"] = 2 * cfg.B * (cfg.Hq + cfg.Hkv) * T * cfg.D * cfg.esize
+    # rope: every tree key row read and written once, and each node's cos/sin written (fp32);
+    # attention_rope: the attention's bytes plus that table, read once
+    kb["rope"] = 2 * cfg.B * cfg.Hkv * T * cfg.D * cfg.esize + cfg.B * T * cfg.D * 4
+    kb["attention_rope"] = kb["attention"] + cfg.B * T * cfg.D * 4
     # commit: each accepted node's K and V rows read and written once, plus the emitted tokens
     moved = int(step.accept_length.cpu().numpy().sum())
     kb["commit"] = 4 * moved * cfg.Hkv * cfg.D * cfg.esize + cfg.B * (step.tree.dims["dmax"] + 1) * 4

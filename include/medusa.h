@@ -269,9 +269,12 @@ int tree_attention(const void* q, const void* k_cache, const void* v_cache, int 
  *     (x_j, x_{j+D/2}) -> (x_j cos - x_{j+D/2} sin,  x_j sin + x_{j+D/2} cos),
  * in fp32 with the angle reduced in fp64, rounded to dtype (nearest even).  The rotated keys
  * are written back into k_cache (call once per step: the prefix rows are taken as already
- * rotated); q is left unchanged (its rotated copy lives in the workspace).  Then exactly
- * tree_attention on the rotated queries and keys.  Arguments, limits and errors as
- * tree_attention, plus rope_base > 1 (10000 for LLaMA-family models).
+ * rotated) by a first kernel; the queries are rotated inside the attention kernel as they are
+ * loaded, and q is left unchanged.  The result is exactly tree_attention on the rotated queries
+ * and keys.  Arguments, limits and errors as tree_attention, plus rope_base > 1 (10000 for
+ * LLaMA-family models).  The workspace (size from tree_attention_rope_workspace, always > 0)
+ * holds every node's cos/sin ([B*T][2][D/2] floats, rounded up to 256 bytes) followed by
+ * tree_attention's own workspace.
  */
 size_t tree_attention_rope_workspace(int B, int Hq, int Hkv, int T, int D, int max_prefix_len);
 int tree_attention_rope(const void* q, void* k_cache, const void* v_cache, int dtype,

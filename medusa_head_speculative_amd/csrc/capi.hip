@@ -337,13 +337,16 @@ int tree_attention(const void* q, const void* k_cache, const void* v_cache, int 
 }
 
 // ---- tree attention with rotary embedding at depth positions ---------------------------------
-static size_t rope_q_bytes(int B, int Hq, int T, int D) {
-  return (static_cast<size_t>(B) * Hq * T * D * sizeof(float) + 255) & ~size_t(255);
+// The tree key rows are rotated in place by their own kernel, which also writes every node's
+// cos/sin to a table [B*T][2][D/2] floats at the start of the workspace; the attention kernel
+// rotates the queries with it as they are loaded.  The attention's own workspace follows.
+static size_t rope_table_bytes(int B, int T, int D) {
+  return (static_cast<size_t>(B) * T * D * sizeof(float) + 255) & ~static_cast<size_t>(255);
 }
 
 size_t tree_attention_rope_workspace(int B, int Hq, int Hkv, int T, int D, int max_prefix_len) {
-  if (attn_shape(B, Hq, Hkv, T, D, max_prefix_len) != MEDUSA_OK) return 0;
-  return rope_q_bytes(B, Hq, T, D) + medusa::attn_plan(1, B, Hq, Hkv, T, D, max_prefix_len).total;
+  const size_t a = tree_attention_workspace(B, Hq, Hkv, T, D, max_prefix_len);
+  return a ? rope_table_bytes(B, T, D) + a : 0;
 }
 
 int tree_attention_rope(const void* q, void* k_cache, const void* v_cache, int dtype,
@@ -360,21 +363,20 @@ int tree_attention_rope(const void* q, void* k_cache, const void* v_cache, int d
   if (!(rope_base > 1.f) || !std::isfinite(rope_base)) return fail(MEDUSA_ERR_ARG, "rope_base = %g, need > 1", rope_base);
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt(static_cast<float>(D));
   if (!std::isfinite(scale)) return fail(MEDUSA_ERR_ARG, "scale is not finite");
-  const size_t qb = rope_q_bytes(B, Hq, T, D);
-  const size_t need = qb + medusa::attn_plan(dtype, B, Hq, Hkv, T, D, max_prefix_len).total;
+  const size_t tab = rope_table_bytes(B, T, D);
+  const size_t need = tab + medusa::attn_plan(dtype, B, Hq, Hkv, T, D, max_prefix_len).total;
   if (!workspace || workspace_bytes < need)
     return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   if ((rc = check_pending())) return rc;
   char* ws = static_cast<char*>(workspace);
+  float* cs = reinterpret_cast<float*>(ws);
   medusa::RopeArgs r{};
-  r.q = q;
-  r.q_rot = ws;
   r.kc = k_cache;
+  r.cs_table = cs;
   r.prefix_len = prefix_len;
   r.pos = position_ids;
   r.base = rope_base;
   r.B = B;
-  r.Hq = Hq;
   r.Hkv = Hkv;
   r.T = T;
   r.D = D;
@@ -382,9 +384,9 @@ int tree_attention_rope(const void* q, void* k_cache, const void* v_cache, int d
   r.lcap = lcap;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((rc = launched(medusa::launch_rope_tree(r, dtype, st), "tree_attention_rope"))) return rc;
-  return launched(medusa::launch_tree_attention(ws, k_cache, v_cache, dtype, prefix_len,
+  return launched(medusa::launch_tree_attention(q, k_cache, v_cache, dtype, prefix_len,
                                                 max_prefix_len, lcap, mask, B, Hq, Hkv, T, D,
-                                                scale, out, ws + qb, st),
+                                                scale, out, ws + tab, st, cs),
                   "tree_attention_rope");
 }
 

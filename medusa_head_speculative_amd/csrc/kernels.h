@@ -53,10 +53,13 @@ struct AttnPlan {
   size_t ws_o, ws_ml, total;
 };
 AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_prefix_len);
+// rope_cs != nullptr: the queries are rotated in the kernel as they are loaded, with the cos/sin
+// table [B*T][2][D/2] of launch_rope_tree; the tree key rows must already be rotated in the cache
 hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, int dtype,
                                  const int32_t* prefix_len, int max_prefix_len, long lcap,
                                  const uint64_t* mask, int B, int Hq, int Hkv, int T, int D,
-                                 float scale, void* out, char* ws, hipStream_t s);
+                                 float scale, void* out, char* ws, hipStream_t s,
+                                 const float* rope_cs = nullptr);
 
 // ---- typical acceptance ------------------------------------------------------------------
 struct AcceptWs {
@@ -99,13 +102,12 @@ hipError_t launch_commit(const CommitArgs& a, int B, hipStream_t s);
 
 // ---- rotary embedding of the tree tokens ----------------------------------------------------
 struct RopeArgs {
-  const void* q;            // [B][Hq][T][D]
-  void* q_rot;              // [B][Hq][T][D], written
   void* kc;                 // [B][Hkv][lcap][D], tree rows rotated in place
   const int32_t* prefix_len;
   const int32_t* pos;       // [B][T]
+  float* cs_table;          // [B*T][2][D/2] cos then sin of every node, written (may be null)
   float base;
-  int B, Hq, Hkv, T, D, Lmax;
+  int B, Hkv, T, D, Lmax;
   long lcap;
 };
 hipError_t launch_rope_tree(const RopeArgs& a, int dtype, hipStream_t s);

@@ -1,21 +1,22 @@
-// Rotary embedding of the tree tokens at their position ids, ahead of tree attention.
+// Rotary embedding of the tree tokens at their position ids, for tree attention.
 //
 // Wiblog "Medusa multi-head speculative decoding", tree-attention section: besides the mask, the
 // position encoding must give every tree token its correct position index: prefix_len + depth,
 // the position it has when its own path is decoded one token at a time (build_tree's
 // position_ids).  The encoding is the rotary one of the LLaMA-family models: dimension i < D/2
 // turns with i + D/2 by the angle pos * base^(-2i/D).  The prefix keys in the cache were rotated
-// when they were written; this kernel rotates the tree tokens' queries (into a buffer) and their
-// key rows in the cache (in place), rounding to the storage type (nearest even for bf16).
+// when they were written; this kernel rotates the tree tokens' key rows in the cache (in place),
+// rounding to the storage type (nearest even for bf16), and writes every tree node's cos/sin to
+// a table from which the attention kernel rotates the queries as it loads them.
 //
-// The rows of one tree node share their angles, so a work-group takes one (sequence, node) and a
-// chunk of up to 32 of its rows (q heads, then kv heads), 8 per wave.  A lane owns 4 consecutive
-// pairs (i, i + D/2) of one row, so a wave instruction covers 64 / (D/8) rows with 8-byte (bf16)
-// or 16-byte (fp32) accesses.  Every wave issues its rows' loads first; meanwhile wave 0 forms
-// the node's D/2 angles and their cos/sin into LDS.  An angle is formed and reduced to [-pi, pi]
-// in fp64 (at position 8192 an fp32 angle would already be off by ~5e-4 rad), from inverse
-// frequencies base^(-2i/D) computed once on the host in fp64; sin/cos and the rotation run in
-// fp32.
+// One wave per (sequence, node, chunk of kv heads): the rows of one node share the angles.  A lane
+// owns 4 consecutive pairs (i, i + D/2) of one row, so a wave instruction covers 64 / (D/8) rows
+// with 8-byte (bf16) or 16-byte (fp32) accesses, and a chunk is kRopeGroups such row groups, all
+// loaded before the angles are formed.  Each lane forms the 4 angles it owns (no LDS, no
+// barrier); the wave of the first chunk also writes the node's cos/sin.  An angle is formed and reduced to
+// [-pi, pi] in fp64 (at position 8192 an fp32 angle would already be off by ~5e-4 rad), from
+// inverse frequencies base^(-2i/D) computed once on the host in fp64; sin/cos and the rotation
+// run in fp32.
 #include <math.h>
 
 #include "common.h"
@@ -24,8 +25,8 @@
 namespace medusa {
 
 constexpr int kRopeThreads = 256;
-constexpr int kRopeRowsPerWg = 32;            // 8 rows per wave
 constexpr unsigned kRopeMaxGrid = 65535;
+constexpr int kRopeGroups = 2;                // row groups of one wave, in flight at once
 
 struct RopeKArgs {
   RopeArgs a;
@@ -54,72 +55,67 @@ __device__ __forceinline__ void rope_store4(void* p, long i, float4 v) {
   }
 }
 
+__device__ __forceinline__ void rope_cs(double p, double inv, float& cs, float& sn) {
+  const double two_pi = 6.283185307179586476925286766559;
+  const double inv_two_pi = 0.15915494309189533576888376337251;
+  const double ang = p * inv;
+  const float red = static_cast<float>(fma(-two_pi, rint(ang * inv_two_pi), ang));
+  sincosf(red, &sn, &cs);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kRopeThreads) void rope_tree_kernel(RopeKArgs k) {
   const RopeArgs& a = k.a;
-  __shared__ __align__(16) float s_cs[64];
-  __shared__ __align__(16) float s_sn[64];
   const int half = a.D / 2;
   const int lpr = half / 4;                                  // lanes per row
   const int rpi = 64 / lpr;                                  // rows per wave instruction
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q4 = (lane % lpr) * 4;                           // this lane's first pair index
-  const int R = a.Hq + a.Hkv;                                // rows of one node
-  const int chunks = (R + kRopeRowsPerWg - 1) / kRopeRowsPerWg;
-  const long items = static_cast<long>(a.B) * a.T * chunks;
-  const double two_pi = 6.283185307179586476925286766559;
-  const double inv_two_pi = 0.15915494309189533576888376337251;
-  for (long it = blockIdx.x; it < items; it += gridDim.x) {
-    const int ch = static_cast<int>(it % chunks);
-    const long bn = it / chunks;
+  const int rsub = lane / lpr;
+  const int chunk = kRopeGroups * rpi;                      // kv heads per wave
+  const int nch = (a.Hkv + chunk - 1) / chunk;
+  const long units = static_cast<long>(a.B) * a.T * nch;
+  for (long u = static_cast<long>(blockIdx.x) * 4 + wave; u < units; u += static_cast<long>(gridDim.x) * 4) {
+    const long bn = u / nch;
+    const int j0 = static_cast<int>(u % nch) * chunk;
     const int b = static_cast<int>(bn / a.T), n = static_cast<int>(bn % a.T);
     const int L = min(max(a.prefix_len[b], 0), a.Lmax);    // as tree attention reads it
-    // this wave's 8 rows: rows ch*32 + wave*8 + g*rpi + lane/lpr, g < 8/rpi
-    constexpr int kMaxG = 2;                               // 8 rows / rpi: 2 for D = 128, 1 for D = 64
-    float4 x[kMaxG], y[kMaxG];
-    long base[kMaxG];
-    void* dst[kMaxG];
+    auto row_base = [&](int j) {                            // kv head j's tree row of this node
+      return ((static_cast<long>(b) * a.Hkv + j) * a.lcap + L + n) * a.D;
+    };
+    {
+      float4 x[kRopeGroups], y[kRopeGroups];
+      long base[kRopeGroups];
 #pragma unroll
-    for (int g = 0; g < kMaxG; ++g) {
-      base[g] = -1;
-      const int j = ch * kRopeRowsPerWg + wave * 8 + g * rpi + lane / lpr;
-      if (g * rpi < 8 && j < R) {
-        const void* src;
-        if (j < a.Hq) {
-          src = a.q;
-          dst[g] = a.q_rot;
-          base[g] = ((static_cast<long>(b) * a.Hq + j) * a.T + n) * a.D;
-        } else {
-          src = a.kc;
-          dst[g] = a.kc;
-          base[g] = ((static_cast<long>(b) * a.Hkv + (j - a.Hq)) * a.lcap + L + n) * a.D;
+      for (int g = 0; g < kRopeGroups; ++g) {
+        const int j = j0 + g * rpi + rsub;
+        base[g] = -1;
+        if (j < a.Hkv) {
+          base[g] = row_base(j);
+          x[g] = rope_load4<BF16>(a.kc, base[g] + q4);
+          y[g] = rope_load4<BF16>(a.kc, base[g] + q4 + half);
         }
-        x[g] = rope_load4<BF16>(src, base[g] + q4);
-        y[g] = rope_load4<BF16>(src, base[g] + q4 + half);
       }
-    }
-    __syncthreads();                                        // the last item's readers are done
-    if (wave == 0 && lane < half) {
-      const double ang = static_cast<double>(a.pos[bn]) * k.inv[lane];
-      const float red = static_cast<float>(fma(-two_pi, rint(ang * inv_two_pi), ang));
-      float sn, cs;
-      sincosf(red, &sn, &cs);
-      s_cs[lane] = cs;
-      s_sn[lane] = sn;
-    }
-    __syncthreads();
-    const float4 cs = *reinterpret_cast<const float4*>(s_cs + q4);
-    const float4 sn = *reinterpret_cast<const float4*>(s_sn + q4);
+      float c[4], s[4];
+      const double p = static_cast<double>(a.pos[bn]);
 #pragma unroll
-    for (int g = 0; g < kMaxG; ++g) {
-      if (base[g] < 0) continue;
-      const float4 xv = x[g], yv = y[g];
-      rope_store4<BF16>(dst[g], base[g] + q4,
-                        make_float4(fmaf(xv.x, cs.x, -(yv.x * sn.x)), fmaf(xv.y, cs.y, -(yv.y * sn.y)),
-                                    fmaf(xv.z, cs.z, -(yv.z * sn.z)), fmaf(xv.w, cs.w, -(yv.w * sn.w))));
-      rope_store4<BF16>(dst[g], base[g] + q4 + half,
-                        make_float4(fmaf(xv.x, sn.x, yv.x * cs.x), fmaf(xv.y, sn.y, yv.y * cs.y),
-                                    fmaf(xv.z, sn.z, yv.z * cs.z), fmaf(xv.w, sn.w, yv.w * cs.w)));
+      for (int e = 0; e < 4; ++e) rope_cs(p, k.inv[q4 + e], c[e], s[e]);
+      if (j0 == 0 && rsub == 0 && a.cs_table) {               // cos/sin of this node for the queries
+        float* t = a.cs_table + bn * 2 * half;
+        *reinterpret_cast<float4*>(t + q4) = make_float4(c[0], c[1], c[2], c[3]);
+        *reinterpret_cast<float4*>(t + half + q4) = make_float4(s[0], s[1], s[2], s[3]);
+      }
+#pragma unroll
+      for (int g = 0; g < kRopeGroups; ++g) {
+        if (base[g] < 0) continue;
+        const float4 xv = x[g], yv = y[g];
+        rope_store4<BF16>(a.kc, base[g] + q4,
+                          make_float4(fmaf(xv.x, c[0], -(yv.x * s[0])), fmaf(xv.y, c[1], -(yv.y * s[1])),
+                                      fmaf(xv.z, c[2], -(yv.z * s[2])), fmaf(xv.w, c[3], -(yv.w * s[3]))));
+        rope_store4<BF16>(a.kc, base[g] + q4 + half,
+                          make_float4(fmaf(xv.x, s[0], yv.x * c[0]), fmaf(xv.y, s[1], yv.y * c[1]),
+                                      fmaf(xv.z, s[2], yv.z * c[2]), fmaf(xv.w, s[3], yv.w * c[3])));
+      }
     }
   }
 }
@@ -129,9 +125,10 @@ hipError_t launch_rope_tree(const RopeArgs& a, int dtype, hipStream_t s) {
   k.a = a;
   for (int i = 0; i < a.D / 2 && i < 64; ++i)
     k.inv[i] = pow(static_cast<double>(a.base), -2.0 * i / a.D);
-  const int R = a.Hq + a.Hkv;
-  const long items = static_cast<long>(a.B) * a.T * ((R + kRopeRowsPerWg - 1) / kRopeRowsPerWg);
-  const unsigned grid = static_cast<unsigned>(items < kRopeMaxGrid ? items : kRopeMaxGrid);
+  const int chunk = kRopeGroups * (64 / (a.D / 8));
+  const long units = static_cast<long>(a.B) * a.T * ((a.Hkv + chunk - 1) / chunk);
+  const long wgs = (units + 3) / 4;
+  const unsigned grid = static_cast<unsigned>(wgs < kRopeMaxGrid ? wgs : kRopeMaxGrid);
   hook_before(K_ROPE, s);
   if (dtype == 1) rope_tree_kernel<true><<<grid, kRopeThreads, 0, s>>>(k);
   else rope_tree_kernel<false><<<grid, kRopeThreads, 0, s>>>(k);

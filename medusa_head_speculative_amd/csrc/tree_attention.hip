@@ -44,7 +44,17 @@ struct AttnArgs {
   long lcap;
   int B, Hq, Hkv, T, W, G, M, Mpad, qtiles, splits, nwork, Lmax;
   float sl2;         // scale * log2(e)
+  const float* rope_cs;  // [B*T][2][D/2] cos, sin of every node; queries are rotated when ROPE is set
 };
+
+// Rotary embedding of one pair (x_i, x_{i+D/2}) with the cos/sin of its angle, in fp32 as the
+// rotation of the key rows does
+__device__ __forceinline__ void rope_rotate(float cs, float sn, float& x, float& y) {
+  const float xr = fmaf(x, cs, -(y * sn));
+  const float yr = fmaf(x, sn, y * cs);
+  x = xr;
+  y = yr;
+}
 
 __device__ __forceinline__ bf16x8_t lds_read16(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
@@ -127,7 +137,7 @@ __device__ __forceinline__ void issue_mask(const uint64_t* __restrict__ mask, in
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(Md + wave * 32), 4, 0, 0);
 }
 
-template <int D>
+template <int D, bool ROPE>
 __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
   constexpr int NKB = D / 32;            // 32-wide contraction blocks over the head dim
   constexpr int NDB = D / 16;            // 16-wide output blocks over the head dim
@@ -217,6 +227,40 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
       qf[mb][kb] = rvalid[mb] ? load_bf16x8(qrow + kb * 32 + 8 * lg) : zero_bf16x8();
+  }
+  if constexpr (ROPE) {
+    // rotary embedding of the queries in registers: fragment kb holds elements
+    // kb*32 + 8*lg + e, so the partner i + D/2 of element i (kb < NKB/2) sits at the same (lg, e)
+    // of fragment kb + NKB/2; the result is rounded to bf16 as a stored rotated query would be
+    constexpr int HKB = NKB / 2;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (!rvalid[mb]) continue;
+      const float* cs = a.rope_cs + (static_cast<long>(b) * a.T + node[mb]) * D;
+#pragma unroll
+      for (int kb = 0; kb < HKB; ++kb) {
+        const float4* cp = reinterpret_cast<const float4*>(cs + kb * 32 + 8 * lg);
+        const float4* sp = reinterpret_cast<const float4*>(cs + D / 2 + kb * 32 + 8 * lg);
+        const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        uint4 lo = __builtin_bit_cast(uint4, qf[mb][kb]);
+        uint4 hi = __builtin_bit_cast(uint4, qf[mb][kb + HKB]);
+        uint32_t* lw = reinterpret_cast<uint32_t*>(&lo);
+        uint32_t* hw = reinterpret_cast<uint32_t*>(&hi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int sh = 16 * (e & 1);
+          float x = bf16_to_f32(static_cast<uint16_t>(lw[e >> 1] >> sh));
+          float y = bf16_to_f32(static_cast<uint16_t>(hw[e >> 1] >> sh));
+          rope_rotate(cv[e], sv[e], x, y);
+          lw[e >> 1] = (lw[e >> 1] & (0xffff0000u >> sh)) | (static_cast<uint32_t>(f32_to_bf16_rne(x)) << sh);
+          hw[e >> 1] = (hw[e >> 1] & (0xffff0000u >> sh)) | (static_cast<uint32_t>(f32_to_bf16_rne(y)) << sh);
+        }
+        qf[mb][kb] = __builtin_bit_cast(bf16x8_t, lo);
+        qf[mb][kb + HKB] = __builtin_bit_cast(bf16x8_t, hi);
+      }
+    }
   }
 
   float mrow[2] = {-INFINITY, -INFINITY};
@@ -479,7 +523,8 @@ __global__ __launch_bounds__(64) void tree_attn_f32(const float* __restrict__ q,
                                                     const int32_t* __restrict__ prefix_len,
                                                     const uint64_t* __restrict__ mask, float* out,
                                                     long lcap, int Hq, int Hkv, int T, int W,
-                                                    int D, float sl2, int Lmax) {
+                                                    int D, float sl2, int Lmax,
+                                                    const float* __restrict__ rope_cs) {
   __shared__ float s_q[128];
   __shared__ float s_p[64];
   const long u = blockIdx.x;
@@ -493,6 +538,17 @@ __global__ __launch_bounds__(64) void tree_attn_f32(const float* __restrict__ q,
   const float* qr = q + u * D;
   for (int d = lane; d < D; d += 64) s_q[d] = qr[d];
   __syncthreads();
+  if (rope_cs) {                           // rotary embedding of the query at its position
+    const int half = D / 2;
+    if (lane < half) {
+      const float* cs = rope_cs + (static_cast<long>(b) * T + i) * D;
+      float x = s_q[lane], y = s_q[lane + half];
+      rope_rotate(cs[lane], cs[half + lane], x, y);
+      s_q[lane] = x;
+      s_q[lane + half] = y;
+    }
+    __syncthreads();
+  }
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
   const long ncols = static_cast<long>(L) + T;
   for (long c0 = 0; c0 < ncols; c0 += 64) {
@@ -595,7 +651,8 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
 hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, int dtype,
                                  const int32_t* prefix_len, int max_prefix_len, long lcap,
                                  const uint64_t* mask, int B, int Hq, int Hkv, int T, int D,
-                                 float scale, void* out, char* ws, hipStream_t s) {
+                                 float scale, void* out, char* ws, hipStream_t s,
+                                 const float* rope_cs) {
   const AttnPlan P = attn_plan(dtype, B, Hq, Hkv, T, D, max_prefix_len);
   const int W = (T + 63) / 64;
   const float sl2 = scale * 1.4426950408889634f;
@@ -603,7 +660,8 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
     hook_before(K_ATTENTION, s);
     tree_attn_f32<<<static_cast<unsigned>(static_cast<long>(B) * Hq * T), 64, 0, s>>>(
         static_cast<const float*>(q), static_cast<const float*>(kc), static_cast<const float*>(vc),
-        prefix_len, mask, static_cast<float*>(out), lcap, Hq, Hkv, T, W, D, sl2, max_prefix_len);
+        prefix_len, mask, static_cast<float*>(out), lcap, Hq, Hkv, T, W, D, sl2, max_prefix_len,
+        rope_cs);
     hook_after(K_ATTENTION, s);
     return hipGetLastError();
   }
@@ -630,10 +688,16 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
   a.nwork = B * Hkv * P.qtiles * P.splits;
   a.sl2 = sl2;
   a.Lmax = max_prefix_len;
+  a.rope_cs = rope_cs;
   const unsigned grid = static_cast<unsigned>(((a.nwork + 7) / 8) * 8);
   hook_before(K_ATTENTION, s);
-  if (D == 128) tree_attn_bf16<128><<<grid, 256, 0, s>>>(a);
-  else tree_attn_bf16<64><<<grid, 256, 0, s>>>(a);
+  if (rope_cs) {
+    if (D == 128) tree_attn_bf16<128, true><<<grid, 256, 0, s>>>(a);
+    else tree_attn_bf16<64, true><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (D == 128) tree_attn_bf16<128, false><<<grid, 256, 0, s>>>(a);
+    else tree_attn_bf16<64, false><<<grid, 256, 0, s>>>(a);
+  }
   hook_after(K_ATTENTION, s);
   if (P.splits > 1) {
     hook_before(K_ATTN_COMBINE, s);

@@ -121,11 +121,16 @@ def test_invalid_arguments_fail_before_any_launch(m):
     ra = [p, p, p, 1, p, 10, 100, p, p]                         # q .. position_ids
     assert L.tree_attention_rope(*ra, 1.0, 1, 4, 4, 9, 64, 0.0, p, p, 1 << 20, None) == -1
     assert L.tree_attention_rope(*ra, 10000.0, 1, 4, 3, 9, 64, 0.0, p, p, 1 << 20, None) == -2
-    assert L.tree_attention_rope(*ra, 10000.0, 1, 4, 4, 9, 64, 0.0, p, p, 16, None) == -5
+    # the 7B attention shape needs split partials, so a 16-byte workspace is short
+    rw = [p, p, p, 1, p, 1024, 1100, p, p]
+    assert L.tree_attention_workspace(1, 32, 32, 65, 128, 1024) > 16
+    assert L.tree_attention_rope(*rw, 10000.0, 1, 32, 32, 65, 128, 0.0, p, p, 16, None) == -5
     assert L.tree_attention_rope(p, p, p, 1, p, 10, 100, p, None, 10000.0, 1, 4, 4, 9, 64, 0.0,
                                  p, p, 1 << 20, None) == -1
-    assert L.tree_attention_rope_workspace(1, 4, 4, 9, 64, 10) > \
-        L.tree_attention_workspace(1, 4, 4, 9, 64, 10)
+    # cos/sin table (65 nodes x 128 floats, rounded up to 256 bytes) ahead of the attention's own
+    assert L.tree_attention_rope_workspace(1, 32, 32, 65, 128, 1024) == \
+        33280 + L.tree_attention_workspace(1, 32, 32, 65, 128, 1024)
+    assert L.tree_attention_rope_workspace(1, 32, 5, 65, 128, 1024) == 0
     hx = [p, p, p, p, p, 1e-5, p]                                # h .. w2
     assert L.medusa_heads_ex(*hx, 0, 1, 1, 64, 100, 1, 2, 1, None, p, None, p, 1 << 20, None) == -3
     assert L.medusa_heads_ex(*hx, 1, 0, 1, 64, 100, 1, 9, 1, None, p, None, p, 1 << 20, None) == -2

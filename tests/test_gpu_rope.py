@@ -82,8 +82,10 @@ def test_rope_attention_full_size(ci, base):
     ("bf16", 64, 3, 4, 4, "c0", [5, 77, 1], "far"),        # positions near 100000
     ("f32", 64, 2, 4, 2, "c3", [40, 0], "depth"),
     ("f32", 128, 1, 2, 1, "c2", [123], "far"),
-    ("f32", 128, 1, 40, 8, "c1", [9], "depth"),        # 48 rows per node: two chunks, ragged
-    ("bf16", 64, 2, 32, 8, "c1", [3, 64], "far"),      # 40 rows per node, 8 rows per instruction
+    ("f32", 128, 1, 40, 8, "c1", [9], "depth"),        # 8 key rows per node: one full chunk
+    ("bf16", 64, 2, 32, 8, "c1", [3, 64], "far"),      # 8 rows per instruction, half a chunk
+    ("bf16", 128, 2, 12, 12, "c0", [17, 250], "depth"),  # 12 rows: a full chunk and a ragged one
+    ("f32", 64, 1, 40, 20, "c3", [31], "far"),         # 20 rows: chunks of 16 and 4
 ])
 def test_rope_attention_edges(dtype, D, B, Hq, Hkv, tree, pls, posmode):
     m = lib()
