@@ -48,13 +48,27 @@ __device__ __forceinline__ float load_elem(const void* p, int dtype, long i) {
   return dtype == 0 ? static_cast<const float*>(p)[i] : bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
 }
 
-// One finished output y = (W x_b)[row] of head k.
-__device__ __forceinline__ void heads_epilogue(const HeadsEpi& ep, int k, long row, int b, float y) {
+// The first layer's per-output inputs: bias b1[k][row] and residual x[b][row] (h or the previous
+// block's r).
+struct EpiIn {
+  float bias, x;
+};
+__device__ __forceinline__ EpiIn epi_inputs(const HeadsEpi& ep, int k, long row, int b) {
+  const int i = static_cast<int>(row);
+  EpiIn in;
+  in.bias = load_elem(ep.b1, ep.dtype, static_cast<long>(weight_head(ep, k)) * ep.hd + i);
+  in.x = ep.r_res ? ep.r_res[(static_cast<long>(b) * ep.K + k) * ep.hd + i]
+                  : load_elem(ep.h, ep.dtype, static_cast<long>(b) * ep.hd + i);
+  return in;
+}
+
+// One finished output y = (W x_b)[row] of head k; `in` holds the first layer's inputs.
+__device__ __forceinline__ void heads_epilogue_in(const HeadsEpi& ep, int k, long row, int b, float y,
+                                                  EpiIn in) {
   if (ep.mode == 0) {
     const int i = static_cast<int>(row);
-    const float u = y + load_elem(ep.b1, ep.dtype, static_cast<long>(weight_head(ep, k)) * ep.hd + i);
-    const float x = ep.r_res ? ep.r_res[(static_cast<long>(b) * ep.K + k) * ep.hd + i]
-                             : load_elem(ep.h, ep.dtype, static_cast<long>(b) * ep.hd + i);
+    const float u = y + in.bias;
+    const float x = in.x;
     const float r = x + u / (1.0f + expf(-u));
     ep.r_out[(static_cast<long>(b) * ep.K + k) * ep.hd + i] = r;
     if (ep.xs) {
@@ -68,6 +82,35 @@ __device__ __forceinline__ void heads_epilogue(const HeadsEpi& ep, int k, long r
   } else {
     ep.logits[(static_cast<long>(b) * ep.K + k) * ep.rows + row] = y;
   }
+}
+
+__device__ __forceinline__ void heads_epilogue(const HeadsEpi& ep, int k, long row, int b, float y) {
+  heads_epilogue_in(ep, k, row, b, y, ep.mode == 0 ? epi_inputs(ep, k, row, b) : EpiIn{0.f, 0.f});
+}
+
+// The same inputs for bf16 heads, loaded early as raw 32-bit words and converted only when used,
+// so that nothing waits for them before the weight stream starts: the aligned word holding the
+// bf16 bias, and the fp32 residual (the previous block's r) or the aligned word holding the bf16
+// h element.  (hd is a multiple of 32, so an element's aligned word lies inside its row.)
+struct EpiRaw {
+  uint32_t bias, x;
+};
+__device__ __forceinline__ EpiRaw epi_raw_bf16(const HeadsEpi& ep, int k, long row, int b) {
+  const long i = row;
+  const long bi = static_cast<long>(weight_head(ep, k)) * ep.hd + i;
+  const uint32_t* xp = ep.r_res ? reinterpret_cast<const uint32_t*>(ep.r_res + (static_cast<long>(b) * ep.K + k) * ep.hd + i)
+                                : reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(ep.h) + ((static_cast<long>(b) * ep.hd + i) & ~1l));
+  EpiRaw in;
+  in.bias = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(ep.b1) + (bi & ~1l));
+  in.x = *xp;
+  return in;
+}
+__device__ __forceinline__ EpiIn epi_from_raw_bf16(const HeadsEpi& ep, long row, EpiRaw r) {
+  // the high half of a word holds the odd element (little endian); row parity is the element's
+  // parity in both arrays since hd is even
+  const int sh = (row & 1) ? 16 : 0;
+  return EpiIn{bf16_to_f32(static_cast<uint16_t>(r.bias >> sh)),
+               ep.r_res ? __uint_as_float(r.x) : bf16_to_f32(static_cast<uint16_t>(r.x >> sh))};
 }
 
 // B operand of v_mfma_f32_16x16x32_bf16 for contraction block kb: lane l holds column n = l%16,
@@ -184,6 +227,7 @@ __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restr
                                                           const uint16_t* __restrict__ xsrc,
                                                           int ncols, HeadsEpi ep) {
   static_assert(KSPLIT == 1 || !PERSIST, "persistent variants own whole items");
+  static_assert(KSPLIT == 1 || TPW <= 2, "the split epilogue gives each thread at most one output");
   __shared__ float red[KSPLIT == 4 ? 4 : 1][TPW][64][4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -229,6 +273,15 @@ __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restr
     f32x4_t acc[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // split epilogue: thread o < 16*TPW*B finishes output (row t0*16 + o/B, sequence o%B); its
+    // first-layer inputs (bf16: this kernel serves only bf16 heads) are loaded now, so their
+    // latency hides behind the weight stream
+    EpiRaw pre{0u, 0u};
+    if (KSPLIT == 4 && ep.mode == 0 && static_cast<int>(threadIdx.x) < 16 * TPW * B) {
+      const int rr = static_cast<int>(threadIdx.x) / B;
+      const long row = t0 * 16 + rr;
+      if (row < ep.rows) pre = epi_raw_bf16(ep, k, row, static_cast<int>(threadIdx.x) - rr * B);
+    }
 
     int kb = kb0;
     for (; kb + U <= kb1; kb += U) {
@@ -264,7 +317,8 @@ __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restr
 #pragma unroll
         for (int j = 0; j < 4; ++j) red[wave][t][lane][j] = acc[t][j];
       __syncthreads();
-      for (int o = threadIdx.x; o < 16 * TPW * B; o += 256) {
+      const int o = threadIdx.x;
+      if (o < 16 * TPW * B) {
         const int rr = o / B, b = o - rr * B;
         const int t = rr >> 4, m = rr & 15;
         const int lh = (m >> 2) * 16 + b, j = m & 3;
@@ -272,7 +326,10 @@ __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restr
 #pragma unroll
         for (int w = 0; w < 4; ++w) y += lo_off ? red[w][t][lh][j] + red[w][t][lh + lo_off][j] : red[w][t][lh][j];
         const long row = t0 * 16 + rr;
-        if (row < ep.rows) heads_epilogue(ep, k, row, b, y);
+        // the opaque step keeps the conversions (and so the wait for the loads) here, after the
+        // weight stream, instead of hoisted next to the loads
+        asm volatile("" : "+v"(pre.bias), "+v"(pre.x));
+        if (row < ep.rows) heads_epilogue_in(ep, k, row, b, y, epi_from_raw_bf16(ep, row, pre));
       }
     } else {
 #pragma unroll
