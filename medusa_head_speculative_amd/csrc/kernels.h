@@ -50,6 +50,7 @@ struct AttnPlan {
   int M;          // query rows per (b, kv head) = G * T
   int qtiles;     // work-group query tiles per (b, kv head)
   int splits;     // KV splits per (b, kv head, q tile)
+  int nmb;        // 16-row blocks per wave of the bf16 kernel (1: 8 waves, 2: 4 waves)
   size_t ws_o, ws_ml, total;
 };
 AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_prefix_len);

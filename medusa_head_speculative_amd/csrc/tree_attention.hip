@@ -5,9 +5,9 @@
 // never across branches; the fixed tree's mask is precomputed.  Ultralytics "Medusa Heads",
 // tree-attention section: each token sees only its ancestors in the tree.
 //
-// bf16 path (matrix cores).  A work-group owns 128 query rows of one (sequence, kv head): the
-// rows are (node, q head of the group) pairs, node-major, so grouped query heads share every
-// K/V tile.  It walks 64-row K/V tiles (the prefix, then the tree rows), staged in LDS row-major:
+// bf16 path (matrix cores).  A work-group owns 128 query rows of one (sequence, kv head), 32 or
+// 16 per wave: the rows are (node, q head of the group) pairs, node-major, so grouped query heads
+// share every K/V tile.  It walks 64-row K/V tiles (the prefix, then the tree rows), staged in LDS row-major:
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q rows held in registers;
 //                 a lane ends up with 4 columns of one query row per 16-column block, so the
 //                 online softmax runs per lane plus two cross-lane steps;
@@ -26,9 +26,17 @@
 
 namespace medusa {
 
-constexpr int kAttnRows = 128;   // query rows per work-group (4 waves x 32)
+constexpr int kAttnRows = 128;   // query rows per work-group (4 waves x 32, or 8 x 16)
 constexpr int kKvTile = 64;
 constexpr int kMaxSplits = 16;
+// Work-groups at or above which the bf16 kernel keeps two row blocks per wave (4 waves of 32
+// rows, 204 VGPRs, two waves per SIMD) instead of one (8 waves of 16 rows, 118 VGPRs, four per
+// SIMD).  Measured on MI355X: the 8-wave form is faster on grids up to a few rounds of the 512
+// work-groups that fit at two per CU (c1 16.2 -> 15.1 us, c2 21.5 -> 20.0, c3 159 -> 155 at 832
+// work-groups), and no faster on the 70B-layer grid of 2240 (1277-1307 against 1293 us; its
+// rotary variant 1264-1283 against 1326-1329), where each wave reading K for only 16 rows
+// doubles the LDS traffic per row.
+constexpr long kAttnTwoBlockUnits = 1536;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 
@@ -110,14 +118,14 @@ __device__ __forceinline__ int v_frag_base(int lg, int mm) {
 
 // Async loads of one 64-row K/V tile straight into LDS (no registers).  Rows past nvalid repeat
 // the last valid row: finite data whose scores the mask removes.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kc,
                                            const uint16_t* __restrict__ vc, long rowbase,
                                            int nvalid, uint16_t* Kd, uint16_t* Vd, int wave,
                                            int lane) {
   constexpr int SLOTS = D / 8;                 // 16-byte chunks per row
   constexpr int RPI = 64 / SLOTS;              // rows per wave instruction
-  constexpr int INST = kKvTile / RPI / 4;      // instructions per wave per matrix
+  constexpr int INST = kKvTile / RPI / NW;     // instructions per wave per matrix
 #pragma unroll
   for (int u = 0; u < INST; ++u) {
     const int rbase = (wave * INST + u) * RPI;
@@ -129,16 +137,27 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kc,
   }
 }
 
-// Async load of the mask words of one tree tile for this wave's 32 query rows straight into LDS
-// (4 bytes per lane: lane l fills half l%2 of row l/2's word).  Invalid rows read node 0's word.
+// Async load of the mask words of one tree tile for this wave's RPW query rows straight into
+// LDS (4 bytes per lane: lane l < 2*RPW fills half l%2 of row l/2's word).  Invalid rows read
+// node 0's word.
+template <int RPW>
 __device__ __forceinline__ void issue_mask(const uint64_t* __restrict__ mask, int W, int tt,
                                            int row_node, uint64_t* Md, int wave, int lane) {
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(mask + static_cast<long>(row_node) * W + tt) + (lane & 1);
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(Md + wave * 32), 4, 0, 0);
+  if (RPW == 32 || lane < 2 * RPW) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(mask + static_cast<long>(row_node) * W + tt) + (lane & 1);
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(Md + wave * RPW), 4, 0, 0);
+  }
 }
 
-template <int D, bool ROPE>
-__global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
+// NMB 16-row blocks per wave and NW = 8 / NMB waves, so a work-group always owns kAttnRows = 128
+// query rows: NMB = 2 keeps more rows per wave, NMB = 1 twice the waves (half the registers each,
+// so four waves share a SIMD).
+template <int D, bool ROPE, int NMB>
+__global__ __launch_bounds__(512 / NMB, 2) void tree_attn_bf16(AttnArgs a) {
+  constexpr int NW = 8 / NMB;            // waves per work-group
+  constexpr int NT = NW * 64;
+  constexpr int RPW = NMB * 16;          // query rows per wave
+  static_assert(NW * RPW == kAttnRows, "a work-group owns kAttnRows rows");
   constexpr int NKB = D / 32;            // 32-wide contraction blocks over the head dim
   constexpr int NDB = D / 16;            // 16-wide output blocks over the head dim
   constexpr int TILE = kKvTile * D;      // elements per K (or V) tile
@@ -174,9 +193,9 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
   //      this work-group reaches the tree rows) ----
   const bool has_tree = t_end > np;
   if (has_tree) {
-    for (int t = tid; t < 64; t += 256) s_active[t] = 0;
+    for (int t = tid; t < 64; t += NT) s_active[t] = 0;
     __syncthreads();
-    for (int p = tid; p < kAttnRows * ntt; p += 256) {
+    for (int p = tid; p < kAttnRows * ntt; p += NT) {
       const int r = p / ntt, t = p - r * ntt;
       const int m = qt * kAttnRows + r;
       if (m < a.M && a.mask[static_cast<long>(m / a.G) * a.W + t] != 0ull) s_active[t] = 1;
@@ -197,10 +216,10 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
     }
   };
 
-  // node whose mask word this lane stages: row wave*32 + lane/2 of the work-group
-  const int mrow_m = qt * kAttnRows + wave * 32 + (lane >> 1);
+  // node whose mask word this lane stages: row wave*RPW + lane/2 of the work-group
+  const int mrow_m = qt * kAttnRows + wave * RPW + (lane >> 1);
   // a wave whose rows are all past M only helps stage tiles and meets the barriers
-  const bool wave_active = qt * kAttnRows + wave * 32 < a.M;
+  const bool wave_active = qt * kAttnRows + wave * RPW < a.M;
   const int mrow_node = mrow_m < a.M ? mrow_m / a.G : 0;
 
   int t = next_active(t_begin);
@@ -209,17 +228,17 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
     long row0;
     int nvalid;
     tile_rows(t, row0, nvalid);
-    issue_tile<D>(a.kc, a.vc, kvbase + row0, nvalid, K0, V0, wave, lane);
-    if (t >= np) issue_mask(a.mask, a.W, t - np, mrow_node, s_mask[0], wave, lane);
+    issue_tile<D, NW>(a.kc, a.vc, kvbase + row0, nvalid, K0, V0, wave, lane);
+    if (t >= np) issue_mask<RPW>(a.mask, a.W, t - np, mrow_node, s_mask[0], wave, lane);
   }
 
-  // ---- this lane's two query rows (mb = 0, 1) ----
-  int node[2];
-  bool rvalid[2];
-  bf16x8_t qf[2][NKB];
+  // ---- this lane's query rows (one per row block mb) ----
+  int node[NMB];
+  bool rvalid[NMB];
+  bf16x8_t qf[NMB][NKB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int m = qt * kAttnRows + wave * 32 + mb * 16 + mm;
+  for (int mb = 0; mb < NMB; ++mb) {
+    const int m = qt * kAttnRows + wave * RPW + mb * 16 + mm;
     rvalid[mb] = m < a.M;
     node[mb] = rvalid[mb] ? m / a.G : 0;
     const int hq = kvh * a.G + (rvalid[mb] ? m % a.G : 0);
@@ -234,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
     // of fragment kb + NKB/2; the result is rounded to bf16 as a stored rotated query would be
     constexpr int HKB = NKB / 2;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
       if (!rvalid[mb]) continue;
       const float* cs = a.rope_cs + (static_cast<long>(b) * a.T + node[mb]) * D;
 #pragma unroll
@@ -263,14 +282,18 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
     }
   }
 
-  float mrow[2] = {-INFINITY, -INFINITY};
+  float mrow[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) mrow[mb] = -INFINITY;
   // row sums of the (bf16) probabilities, accumulated on the matrix cores: P^T times a block of
   // ones gives every lane the sum of its own query row in all four entries
-  f32x4_t lacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
-  f32x4_t oacc[2][NDB];
+  f32x4_t lacc[NMB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < NMB; ++mb) lacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  f32x4_t oacc[NMB][NDB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -286,18 +309,20 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
     // visible columns of this lane's two rows: the staged mask word (tree tiles) and the valid
     // rows of the tile; read from LDS, so nothing here waits for the next tile's loads
     const uint64_t vmask = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
-    uint64_t mw[2] = {vmask, vmask};
+    uint64_t mw[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) mw[mb] = vmask;
     if (is_tree) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) mw[mb] &= s_mask[buf][wave * 32 + mb * 16 + mm];
+      for (int mb = 0; mb < NMB; ++mb) mw[mb] &= s_mask[buf][wave * RPW + mb * 16 + mm];
     }
     const int tn = next_active(t + 1);
     if (tn < t_end) {
       long nrow0;
       int nnvalid;
       tile_rows(tn, nrow0, nnvalid);
-      issue_tile<D>(a.kc, a.vc, kvbase + nrow0, nnvalid, Kn, Vn, wave, lane);
-      if (tn >= np) issue_mask(a.mask, a.W, tn - np, mrow_node, s_mask[buf ^ 1], wave, lane);
+      issue_tile<D, NW>(a.kc, a.vc, kvbase + nrow0, nnvalid, Kn, Vn, wave, lane);
+      if (tn >= np) issue_mask<RPW>(a.mask, a.W, tn - np, mrow_node, s_mask[buf ^ 1], wave, lane);
     }
     if (!wave_active) {
       t = tn;
@@ -306,9 +331,9 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
     }
 
     // ---- scores S^T = K Q^T ----
-    f32x4_t sacc[2][4];
+    f32x4_t sacc[NMB][4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) sacc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     int kb_base = k_frag_base<D>(lg, mm);
@@ -319,16 +344,16 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
       for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8_t kf = lds_read16(Kc + ((kb_base ^ (kb << 5)) + cb * 16 * D));
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sacc[mb][cb] = mfma16x16x32(kf, qf[mb][kb], sacc[mb][cb]);
+        for (int mb = 0; mb < NMB; ++mb) sacc[mb][cb] = mfma16x16x32(kf, qf[mb][kb], sacc[mb][cb]);
       }
     }
 
     // ---- mask, online softmax (log2 domain), P as the B operand of the second product.
     //      The running max is raised lazily: p = 2^(s*scale - m) with s*scale <= m + 8, so the
     //      rescale of O and l (exact either way) runs only when the max grows by more than 8. ----
-    uint32_t pb[2][2][4];   // [mb][ks][dword] packed bf16 pairs
+    uint32_t pb[NMB][2][4];   // [mb][ks][dword] packed bf16 pairs
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
       float sv[4][4];
       if (full) {
 #pragma unroll
@@ -397,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
         const s16x8_t vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         const bf16x8_t va = __builtin_bit_cast(bf16x8_t, vv);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < NMB; ++mb) {
           const uint4 bv = make_uint4(pb[mb][ks][0], pb[mb][ks][1], pb[mb][ks][2], pb[mb][ks][3]);
           oacc[mb][db] = mfma16x16x32(va, __builtin_bit_cast(bf16x8_t, bv), oacc[mb][db]);
         }
@@ -406,7 +431,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < NMB; ++mb) {
         const uint4 bv = make_uint4(pb[mb][ks][0], pb[mb][ks][1], pb[mb][ks][2], pb[mb][ks][3]);
         lacc[mb] = mfma16x16x32(ones, __builtin_bit_cast(bf16x8_t, bv), lacc[mb]);
       }
@@ -425,9 +450,9 @@ __global__ __launch_bounds__(256, 2) void tree_attn_bf16(AttnArgs a) {
 
   // ---- finish: full row sums, then the output or this split's partial ----
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < NMB; ++mb) {
     const float l = lacc[mb][0];
-    const int m = qt * kAttnRows + wave * 32 + mb * 16 + mm;
+    const int m = qt * kAttnRows + wave * RPW + mb * 16 + mm;
     if (!rvalid[mb]) continue;
     if (a.splits == 1) {
       const float inv = 1.f / l;
@@ -639,6 +664,7 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
       p.splits = s < 1 ? 1 : static_cast<int>(s);
     }
   }
+  p.nmb = static_cast<long>(B) * Hkv * p.qtiles * p.splits >= kAttnTwoBlockUnits ? 2 : 1;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
   const size_t rows = static_cast<size_t>(p.splits) * B * Hkv * p.qtiles * kAttnRows;
@@ -691,12 +717,22 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
   a.rope_cs = rope_cs;
   const unsigned grid = static_cast<unsigned>(((a.nwork + 7) / 8) * 8);
   hook_before(K_ATTENTION, s);
-  if (rope_cs) {
-    if (D == 128) tree_attn_bf16<128, true><<<grid, 256, 0, s>>>(a);
-    else tree_attn_bf16<64, true><<<grid, 256, 0, s>>>(a);
+  if (P.nmb == 1) {
+    if (rope_cs) {
+      if (D == 128) tree_attn_bf16<128, true, 1><<<grid, 512, 0, s>>>(a);
+      else tree_attn_bf16<64, true, 1><<<grid, 512, 0, s>>>(a);
+    } else {
+      if (D == 128) tree_attn_bf16<128, false, 1><<<grid, 512, 0, s>>>(a);
+      else tree_attn_bf16<64, false, 1><<<grid, 512, 0, s>>>(a);
+    }
   } else {
-    if (D == 128) tree_attn_bf16<128, false><<<grid, 256, 0, s>>>(a);
-    else tree_attn_bf16<64, false><<<grid, 256, 0, s>>>(a);
+    if (rope_cs) {
+      if (D == 128) tree_attn_bf16<128, true, 2><<<grid, 256, 0, s>>>(a);
+      else tree_attn_bf16<64, true, 2><<<grid, 256, 0, s>>>(a);
+    } else {
+      if (D == 128) tree_attn_bf16<128, false, 2><<<grid, 256, 0, s>>>(a);
+      else tree_attn_bf16<64, false, 2><<<grid, 256, 0, s>>>(a);
+    }
   }
   hook_after(K_ATTENTION, s);
   if (P.splits > 1) {

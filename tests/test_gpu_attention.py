@@ -68,7 +68,10 @@ CASES = [
     ("bf16", 2, 16, 2, 64, "c2", [127, 300]),
     ("bf16", 1, 8, 8, 128, "c4", [5]),
     ("bf16", 1, 4, 1, 128, "chain8", [700]),
-    ("bf16", 1, 16, 1, 64, "c3", [90]),           # 2064 query rows: 9 tiles of 8 waves
+    ("bf16", 1, 16, 1, 64, "c3", [90]),           # 2064 query rows: 17 tiles, the last of 16 rows
+    # 3 x 8 x 70 = 1680 work-groups: the 4-wave, two-row-block form of the kernel
+    ("bf16", 3, 64, 8, 128, "c4", [3, 40, 64]),
+    ("bf16", 3, 64, 8, 64, "c4", [0, 17, 65]),
     ("bf16", 2, 4, 4, 128, "one", [0, 3]),
     ("f32", 2, 4, 2, 64, "c1", [0, 77]),
     ("f32", 1, 2, 2, 128, "c0", [1]),
