@@ -13,7 +13,7 @@
 // handoff is a kernel boundary):
 //   accept_chunks  one work-group per (sequence, internal row, chunk) computes in a single pass
 //                  the chunk's max y, S = sum 2^(y - max) and A = sum (y - max) 2^(y - max) with
-//                  y = l * log2(e) / T, plus the argmax (a chunk is 1 or 2 rounds of 8 elements
+//                  y = l * log2(e) / T, plus the argmax (a chunk is 1 to 8 rounds of 8 elements
 //                  per thread, see accept_unroll);
 //   accept_rows    one work-group per (sequence, internal row) merges the row's partials in chunk
 //                  order, so H = ln2 * (log2 S - A / S) and ln p(x) = ln2 * (y_x - max - log2 S),
@@ -21,6 +21,7 @@
 //   accept_paths   one work-group per sequence scans the paths for the longest accepted prefix
 //                  and finds the next token.
 #include <math.h>
+#include <stdlib.h>
 
 #include "common.h"
 #include "kernels.h"
@@ -32,14 +33,22 @@ constexpr int kAccPerThread = 8;
 constexpr int kAccVec = kAccThreads * kAccPerThread;    // elements per load round of a work-group
 constexpr long kPathWideBytes = 32 << 10;   // leaf rows above this size get a 1024-thread block
 constexpr int kMaxTreeTokens = 4096;
-constexpr long kAccTargetGroups = 2048;
-// Rounds of kAccVec elements per work-group of accept_chunks: 2 when that still leaves at least
-// kAccTargetGroups work-groups, else 1 (small problems stay spread over many CUs).  Measured on
-// MI355X: the 70B-layer rows took 68 us at 2 rounds against 70 at 4 and 75 at 8; the 33B rows
-// 34 us at 2 or 4; the 7B rows (512 work-groups) 14.6 us at 1 against 15.7 at 2.
+// Rounds of kAccVec elements per work-group of accept_chunks: the largest U of 8, 4, 2 that still
+// leaves at least 1024 work-groups (2048 when there are more than 256 rows), else 1.  Fitted to
+// timings on MI355X once every round's loads were in flight together (event-timed acceptance,
+// U = 1 / 2 / 4 / 8): 7B rows (32) 14.2 / 14.6 / 15.7 / 18.6 us; Llama-8B rows (37 of 128256)
+// 18.5 / 17.0 / 17.6 / 19.7; 33B rows (352 of 32000) 30.2 / 27.4 / 28.5 / 29.3; 70B-layer rows
+// (444 of 128256) 75 / 56.6 / 54.4 / 57.6.  MEDUSA_ACCEPT_UNROLL = 1, 2, 4 or 8 overrides it.
 static int accept_unroll(int B, long V, int n_int) {
-  const long C = (V + static_cast<long>(kAccVec) * 2 - 1) / (static_cast<long>(kAccVec) * 2);
-  return C * n_int * B >= kAccTargetGroups ? 2 : 1;
+  static const int forced = [] { const char* v = getenv("MEDUSA_ACCEPT_UNROLL"); return v ? atoi(v) : 0; }();
+  if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced;
+  const long rows = static_cast<long>(n_int) * B;
+  const long target = rows <= 256 ? 1024 : 2048;
+  for (int u = 8; u >= 2; u >>= 1) {
+    const long C = (V + static_cast<long>(kAccVec) * u - 1) / (static_cast<long>(kAccVec) * u);
+    if (C * rows >= target) return u;
+  }
+  return 1;
 }
 
 struct RowStat {   // partial softmax statistics of a set of elements (log2 units)
@@ -113,6 +122,53 @@ __device__ __forceinline__ void load8(const void* row, int dtype, long idx0, lon
   }
 }
 
+// Vector loads (used when V % 8 == 0 and the logits are 16-byte aligned, so the 8 elements a
+// thread takes in a round are either all in the row or all past it).  A round past the row
+// loads the row's first 8 elements instead, an address that is always valid, and is marked
+// invalid, so no branch surrounds a load: all of a thread's rounds are in flight before the
+// first is converted.  (The branchy load8 above makes each round wait for the previous one.)
+// LOAD: 1 = bf16, 2 = fp32.
+template <int LOAD>
+__device__ __forceinline__ void load_vec8(const void* row, long idx0, long V, uint32_t (&w)[8],
+                                          bool& in) {
+  in = idx0 < V;
+  const long i = in ? idx0 : 0;
+  if constexpr (LOAD == 1) {
+    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + i);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    w[4] = w[5] = w[6] = w[7] = 0u;
+  } else {
+    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const float*>(row) + i);
+    const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const float*>(row) + i + 4);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  }
+}
+template <int LOAD>
+__device__ __forceinline__ void unpack_vec8(const uint32_t (&w)[8], bool in, float* x, bool* valid) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    valid[e] = in;
+    x[e] = LOAD == 1 ? bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)))) : __uint_as_float(w[e]);
+  }
+}
+// U rounds of 8 elements at idx0, idx0 + step, ...: LOAD 0 = the general per-round form
+template <int LOAD, int U>
+__device__ __forceinline__ void load_rounds(const void* row, int dtype, long idx0, long step, long V,
+                                            float (&x)[U][8], bool (&valid)[U][8]) {
+  if constexpr (LOAD == 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) load8(row, dtype, idx0 + u * step, V, x[u], valid[u]);
+  } else {
+    uint32_t w[U][8];
+    bool in[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_vec8<LOAD>(row, idx0 + u * step, V, w[u], in[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) unpack_vec8<LOAD>(w[u], in[u], x[u], valid[u]);
+  }
+}
+
 struct AcceptArgs {
   const void* logits;
   int dtype, B, T;
@@ -165,7 +221,7 @@ __device__ __forceinline__ void block_merge(RowStat& st, uint64_t& arg, bool gre
 // Kernel 1, grid (C, n_int, B): statistics and argmax of one chunk (U rounds of 2048 elements)
 // of an internal row, written to the partial arrays.  All U rounds of loads are issued before
 // any is used.
-template <int U>
+template <int U, int LOAD>
 __global__ __launch_bounds__(kAccThreads) void accept_chunks(AcceptArgs a) {
   __shared__ RowStat s_stat[kAccThreads / 64];
   __shared__ uint64_t s_arg[kAccThreads / 64];
@@ -176,8 +232,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_chunks(AcceptArgs a) {
   const long base = static_cast<long>(c) * kAccVec * U + static_cast<long>(threadIdx.x) * kAccPerThread;
   float x[U][kAccPerThread];
   bool valid[U][kAccPerThread];
-#pragma unroll
-  for (int u = 0; u < U; ++u) load8(row, a.dtype, base + u * kAccVec, a.V, x[u], valid[u]);
+  load_rounds<LOAD, U>(row, a.dtype, base, kAccVec, a.V, x, valid);
   uint64_t arg = 0;
   RowStat st{-INFINITY, 0.f, 0.f, 0.f};
   if ((c + 1) * static_cast<long>(kAccVec) * U <= a.V) {
@@ -255,7 +310,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_chunks(AcceptArgs a) {
 // per thread in flight.  Each thread keeps its best value and index with float compares in
 // increasing index order (the first maximum wins; -0 == +0) and keys them once at the end; a
 // thread with no element of the row contributes key 0.
-template <int NT, int UR>
+template <int NT, int UR, int LOAD>
 __device__ __forceinline__ uint64_t block_row_argmax(const void* row, int dtype, long V,
                                                      uint64_t* scratch) {
   constexpr long kStep = static_cast<long>(NT) * kAccPerThread;
@@ -264,8 +319,7 @@ __device__ __forceinline__ uint64_t block_row_argmax(const void* row, int dtype,
   for (long j0 = static_cast<long>(threadIdx.x) * kAccPerThread; j0 < V; j0 += UR * kStep) {
     float x[UR][kAccPerThread];
     bool valid[UR][kAccPerThread];
-#pragma unroll
-    for (int u = 0; u < UR; ++u) load8(row, dtype, j0 + u * kStep, V, x[u], valid[u]);
+    load_rounds<LOAD, UR>(row, dtype, j0, kStep, V, x, valid);
     if (bidx < 0) {                                   // this thread's first element (j0 < V)
       best = x[0][0];
       bidx = j0;
@@ -354,7 +408,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
 // Kernel 3, grid (B): the longest accepted prefix over the paths, and the next token.  When the
 // last accepted node is a leaf, its row's argmax is read here by the whole block with 8 rounds
 // of loads in flight per thread (NT = 1024 for rows above 32 KB: 128 KB at a time; else 256).
-template <int NT>
+template <int NT, int LOAD>
 __global__ __launch_bounds__(NT) void accept_paths(AcceptArgs a) {
   constexpr int kPathThreads = NT;
   constexpr int kPathRegs = 8;                        // path nodes held in registers
@@ -425,7 +479,7 @@ __global__ __launch_bounds__(NT) void accept_paths(AcceptArgs a) {
   } else {
     const int esz = a.dtype == 1 ? 2 : 4;
     const char* lrow = static_cast<const char*>(a.logits) + (static_cast<long>(b) * a.T + last) * a.V * esz;
-    const uint64_t g = block_row_argmax<kPathThreads, 8>(lrow, a.dtype, a.V, s_scratch);
+    const uint64_t g = block_row_argmax<kPathThreads, 8, LOAD>(lrow, a.dtype, a.V, s_scratch);
     if (threadIdx.x == 0) a.next_token[b] = static_cast<int32_t>(sel_key_index(g));
   }
 }
@@ -482,15 +536,26 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, lo
   a.next_token = next_token;
   const dim3 grid(L.chunks, n_internal, B);
   hook_before(K_ACCEPT, s);
-  switch (L.unroll) {
-    case 2: accept_chunks<2><<<grid, kAccThreads, 0, s>>>(a); break;
-    default: accept_chunks<1><<<grid, kAccThreads, 0, s>>>(a); break;
+  // vector loads when every thread's 8-element group is wholly in or out of the row
+  const bool vec = V % 8 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+  const int load = vec ? (dtype == 1 ? 1 : 2) : 0;
+  const bool wide = V * (dtype == 1 ? 2 : 4) > kPathWideBytes;
+#define MEDUSA_ACCEPT_LAUNCH(LD)                                                    \
+  if (L.unroll == 8) accept_chunks<8, LD><<<grid, kAccThreads, 0, s>>>(a);        \
+  else if (L.unroll == 4) accept_chunks<4, LD><<<grid, kAccThreads, 0, s>>>(a);   \
+  else if (L.unroll == 2) accept_chunks<2, LD><<<grid, kAccThreads, 0, s>>>(a);   \
+  else accept_chunks<1, LD><<<grid, kAccThreads, 0, s>>>(a);                      \
+  accept_rows<<<dim3(n_internal, B), kAccThreads, 0, s>>>(a);                      \
+  if (wide) accept_paths<1024, LD><<<B, 1024, 0, s>>>(a);                          \
+  else accept_paths<256, LD><<<B, 256, 0, s>>>(a);
+  if (load == 1) {
+    MEDUSA_ACCEPT_LAUNCH(1)
+  } else if (load == 2) {
+    MEDUSA_ACCEPT_LAUNCH(2)
+  } else {
+    MEDUSA_ACCEPT_LAUNCH(0)
   }
-  accept_rows<<<dim3(n_internal, B), kAccThreads, 0, s>>>(a);
-  if (V * (dtype == 1 ? 2 : 4) > kPathWideBytes)
-    accept_paths<1024><<<B, 1024, 0, s>>>(a);
-  else
-    accept_paths<256><<<B, 256, 0, s>>>(a);
+#undef MEDUSA_ACCEPT_LAUNCH
   hook_after(K_ACCEPT, s);
   return hipGetLastError();
 }

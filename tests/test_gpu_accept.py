@@ -76,14 +76,17 @@ def test_accept_full_size(ci, temp):
 @pytest.mark.parametrize("V,tree,B,temp", [
     (1, "one", 1, 0.7), (7, "c0", 2, 0.7), (2047, "c1", 3, 1.0), (2049, "c1", 3, 0.0),
     (5000, "chain6", 2, 0.7), (4100, "c3", 5, 0.3), (300, "c2", 8, 3.0),
-    (20001, "c4", 5, 0.7),      # 8 load rounds per chunk, ragged last chunk and vector tail
+    (20001, "c4", 5, 0.7),      # 555 rows: 2 rounds per chunk, element loads (V % 8 != 0)
+    (131072, "chain8", 16, 0.7),   # 128 rows: 8 rounds per chunk, vector loads
+    (131077, "chain8", 16, 0.0),   # 8 rounds per chunk, element loads, ragged last chunk
 ])
 def test_accept_edges(dtype, V, tree, B, temp):
     m = lib()
     if tree == "one":
         choices, K, topk = [[0]], 1, 1
-    elif tree == "chain6":
-        choices, K, topk = cartesian_choices([1] * 6), 6, 1
+    elif tree in ("chain6", "chain8"):
+        depth = int(tree[5:])
+        choices, K, topk = cartesian_choices([1] * depth), depth, 1
     else:
         choices, K, topk = load_tree_choices(tree), 5, 10
     topk = min(topk, V)
