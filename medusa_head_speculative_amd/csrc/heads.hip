@@ -449,10 +449,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_chunks(const float* __restr
   const float* x = logits + static_cast<long>(row) * V;
   uint64_t keys[kTopkPerLane];
   const long base = static_cast<long>(c) * kTopkChunk + wave * (kTopkChunk / 4);
+  // every load goes out before any is used: an element past the row loads element 0 instead
+  // (always valid) and is dropped, so no branch surrounds a load
+  float v[kTopkPerLane];
 #pragma unroll
   for (int e = 0; e < kTopkPerLane; ++e) {
     const long idx = base + e * 64 + lane;
-    keys[e] = idx < V ? sel_key(x[idx], static_cast<uint32_t>(idx)) : 0ull;
+    v[e] = x[idx < V ? idx : 0];
+  }
+#pragma unroll
+  for (int e = 0; e < kTopkPerLane; ++e) {
+    const long idx = base + e * 64 + lane;
+    keys[e] = idx < V ? sel_key(v[e], static_cast<uint32_t>(idx)) : 0ull;
   }
   s_cand[wave][lane] = wave_select(keys, 0ull, k);
   __syncthreads();
@@ -502,38 +510,91 @@ __device__ __forceinline__ float block_sum256(float v, float* s_red) {
   return t;
 }
 
+// 8 elements i0, i0 + 256, ... of a row, every load issued before any is converted (a slot past
+// hd reads element 0, always valid, and is ignored by the caller)
+template <bool BF16>
+__device__ __forceinline__ void ln_load8(const void* p, int i0, int hd, float (&v)[8]) {
+  uint32_t raw[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int i = i0 + e * 256;
+    const int ii = i < hd ? i : 0;
+    raw[e] = BF16 ? static_cast<uint32_t>(static_cast<const uint16_t*>(p)[ii])
+                  : __float_as_uint(static_cast<const float*>(p)[ii]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = BF16 ? bf16_to_f32(static_cast<uint16_t>(raw[e])) : __uint_as_float(raw[e]);
+}
+
+// XBF16: the input row is bf16 (h of a bf16 head), else fp32 (h of an fp32 head, or the previous
+// block's r); WBF16: gamma and beta are bf16.
+template <bool XBF16, bool WBF16>
+__device__ __forceinline__ void layernorm_row(const void* x, const void* gamma, const void* beta,
+                                              float eps, int B, int K, int hd, int b, int k,
+                                              long wb, uint16_t* xs, float* xn, float* s_red) {
+  float sum = 0.f;
+  for (int i0 = threadIdx.x; i0 < hd; i0 += 8 * 256) {
+    float v[8];
+    ln_load8<XBF16>(x, i0, hd, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (i0 + e * 256 < hd) sum += v[e];
+  }
+  const float mean = block_sum256(sum, s_red) / static_cast<float>(hd);
+  float sq = 0.f;
+  for (int i0 = threadIdx.x; i0 < hd; i0 += 8 * 256) {
+    float v[8];
+    ln_load8<XBF16>(x, i0, hd, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = v[e] - mean;
+      if (i0 + e * 256 < hd) sq = fmaf(d, d, sq);
+    }
+  }
+  const float var = block_sum256(sq, s_red) / static_cast<float>(hd);
+  const float rstd = 1.0f / sqrtf(var + eps);
+  const char* g = static_cast<const char*>(gamma) + wb * (WBF16 ? 2 : 4);
+  const char* be = static_cast<const char*>(beta) + wb * (WBF16 ? 2 : 4);
+  for (int i0 = threadIdx.x; i0 < hd; i0 += 8 * 256) {
+    float v[8], gv[8], bv[8];
+    ln_load8<XBF16>(x, i0, hd, v);
+    ln_load8<WBF16>(g, i0, hd, gv);
+    ln_load8<WBF16>(be, i0, hd, bv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = i0 + e * 256;
+      if (i >= hd) continue;
+      const float y = (v[e] - mean) * rstd * gv[e] + bv[e];
+      if (xs) {
+        const uint16_t hi = f32_to_bf16_rne(y);
+        const uint16_t lo = f32_to_bf16_rne(y - bf16_to_f32(hi));
+        uint16_t* base = xs + static_cast<long>(k) * 2 * B * hd + i;
+        base[static_cast<long>(b) * hd] = hi;
+        base[static_cast<long>(B + b) * hd] = lo;
+      } else {
+        xn[(static_cast<long>(b) * K + k) * hd + i] = y;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void heads_layernorm(const void* h, const float* r_in, int dtype,
                                                        const void* gamma, const void* beta, float eps,
                                                        int B, int K, int hd, int wh_mul, int blk,
                                                        uint16_t* xs, float* xn) {
   __shared__ float s_red[4];
   const int b = blockIdx.x, k = blockIdx.y;
-  auto xval = [&](int i) {
-    return r_in ? r_in[(static_cast<long>(b) * K + k) * hd + i]
-                : load_elem(h, dtype, static_cast<long>(b) * hd + i);
-  };
-  float sum = 0.f;
-  for (int i = threadIdx.x; i < hd; i += 256) sum += xval(i);
-  const float mean = block_sum256(sum, s_red) / static_cast<float>(hd);
-  float sq = 0.f;
-  for (int i = threadIdx.x; i < hd; i += 256) {
-    const float d = xval(i) - mean;
-    sq = fmaf(d, d, sq);
-  }
-  const float var = block_sum256(sq, s_red) / static_cast<float>(hd);
-  const float rstd = 1.0f / sqrtf(var + eps);
   const long wb = static_cast<long>(k * wh_mul + blk) * hd;
-  for (int i = threadIdx.x; i < hd; i += 256) {
-    const float y = (xval(i) - mean) * rstd * load_elem(gamma, dtype, wb + i) + load_elem(beta, dtype, wb + i);
-    if (xs) {
-      const uint16_t hi = f32_to_bf16_rne(y);
-      const uint16_t lo = f32_to_bf16_rne(y - bf16_to_f32(hi));
-      uint16_t* base = xs + static_cast<long>(k) * 2 * B * hd + i;
-      base[static_cast<long>(b) * hd] = hi;
-      base[static_cast<long>(B + b) * hd] = lo;
-    } else {
-      xn[(static_cast<long>(b) * K + k) * hd + i] = y;
-    }
+  if (r_in) {
+    const float* x = r_in + (static_cast<long>(b) * K + k) * hd;
+    if (dtype == 1) layernorm_row<false, true>(x, gamma, beta, eps, B, K, hd, b, k, wb, xs, xn, s_red);
+    else layernorm_row<false, false>(x, gamma, beta, eps, B, K, hd, b, k, wb, xs, xn, s_red);
+  } else if (dtype == 1) {
+    const uint16_t* x = static_cast<const uint16_t*>(h) + static_cast<long>(b) * hd;
+    layernorm_row<true, true>(x, gamma, beta, eps, B, K, hd, b, k, wb, xs, xn, s_red);
+  } else {
+    const float* x = static_cast<const float*>(h) + static_cast<long>(b) * hd;
+    layernorm_row<false, false>(x, gamma, beta, eps, B, K, hd, b, k, wb, xs, xn, s_red);
   }
 }
 

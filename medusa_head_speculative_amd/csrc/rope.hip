@@ -33,15 +33,22 @@ struct RopeKArgs {
   double inv[64];                             // base^(-2i/D), i < D/2
 };
 
-// 4 consecutive elements at element offset i (a multiple of 4)
+// 4 consecutive elements at element offset i (a multiple of 4), as raw bits (bf16: the low two
+// words) so that every load of a thread is issued before any is converted
 template <bool BF16>
-__device__ __forceinline__ float4 rope_load4(const void* p, long i) {
+__device__ __forceinline__ uint4 rope_load4(const void* p, long i) {
   if (BF16) {
     const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    return make_uint4(v.x, v.y, 0u, 0u);
+  }
+  return *reinterpret_cast<const uint4*>(static_cast<const float*>(p) + i);
+}
+template <bool BF16>
+__device__ __forceinline__ float4 rope_unpack4(uint4 v) {
+  if (BF16)
     return make_float4(bf16_to_f32(static_cast<uint16_t>(v.x)), bf16_to_f32(static_cast<uint16_t>(v.x >> 16)),
                        bf16_to_f32(static_cast<uint16_t>(v.y)), bf16_to_f32(static_cast<uint16_t>(v.y >> 16)));
-  }
-  return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
 template <bool BF16>
 __device__ __forceinline__ void rope_store4(void* p, long i, float4 v) {
@@ -84,17 +91,17 @@ __global__ __launch_bounds__(kRopeThreads) void rope_tree_kernel(RopeKArgs k) {
       return ((static_cast<long>(b) * a.Hkv + j) * a.lcap + L + n) * a.D;
     };
     {
-      float4 x[kRopeGroups], y[kRopeGroups];
+      // every row group's loads go out before any is used; a lane past the last kv head loads
+      // head 0's row (always valid) and stores nothing
+      uint4 xr[kRopeGroups], yr[kRopeGroups];
       long base[kRopeGroups];
 #pragma unroll
       for (int g = 0; g < kRopeGroups; ++g) {
         const int j = j0 + g * rpi + rsub;
-        base[g] = -1;
-        if (j < a.Hkv) {
-          base[g] = row_base(j);
-          x[g] = rope_load4<BF16>(a.kc, base[g] + q4);
-          y[g] = rope_load4<BF16>(a.kc, base[g] + q4 + half);
-        }
+        base[g] = row_base(j < a.Hkv ? j : 0);
+        xr[g] = rope_load4<BF16>(a.kc, base[g] + q4);
+        yr[g] = rope_load4<BF16>(a.kc, base[g] + q4 + half);
+        if (j >= a.Hkv) base[g] = -1;
       }
       float c[4], s[4];
       const double p = static_cast<double>(a.pos[bn]);
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_tree_kernel(RopeKArgs k) {
 #pragma unroll
       for (int g = 0; g < kRopeGroups; ++g) {
         if (base[g] < 0) continue;
-        const float4 xv = x[g], yv = y[g];
+        const float4 xv = rope_unpack4<BF16>(xr[g]), yv = rope_unpack4<BF16>(yr[g]);
         rope_store4<BF16>(a.kc, base[g] + q4,
                           make_float4(fmaf(xv.x, c[0], -(yv.x * s[0])), fmaf(xv.y, c[1], -(yv.y * s[1])),
                                       fmaf(xv.z, c[2], -(yv.z * s[2])), fmaf(xv.w, c[3], -(yv.w * s[3]))));

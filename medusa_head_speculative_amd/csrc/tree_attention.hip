@@ -195,10 +195,24 @@ __global__ __launch_bounds__(512 / NMB, 2) void tree_attn_bf16(AttnArgs a) {
   if (has_tree) {
     for (int t = tid; t < 64; t += NT) s_active[t] = 0;
     __syncthreads();
-    for (int p = tid; p < kAttnRows * ntt; p += NT) {
-      const int r = p / ntt, t = p - r * ntt;
-      const int m = qt * kAttnRows + r;
-      if (m < a.M && a.mask[static_cast<long>(m / a.G) * a.W + t] != 0ull) s_active[t] = 1;
+    // four mask words per thread in flight at once (a slot past the rows reads word 0, always
+    // valid, and is ignored)
+    for (int p0 = tid; p0 < kAttnRows * ntt; p0 += 4 * NT) {
+      uint64_t w[4];
+      int tt[4];
+      bool ok[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = p0 + u * NT;
+        const int r = p / ntt;
+        tt[u] = p - r * ntt;
+        const int m = qt * kAttnRows + r;
+        ok[u] = p < kAttnRows * ntt && m < a.M;
+        w[u] = a.mask[ok[u] ? static_cast<long>(m / a.G) * a.W + tt[u] : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (ok[u] && w[u] != 0ull) s_active[tt[u]] = 1;
     }
     __syncthreads();
   }

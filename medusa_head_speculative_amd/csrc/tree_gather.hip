@@ -18,9 +18,13 @@ __global__ __launch_bounds__(256) void tree_gather(const int32_t* __restrict__ t
   const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= static_cast<long>(B) * T) return;
   const int b = static_cast<int>(i / T), n = static_cast<int>(i - static_cast<long>(b) * T);
-  const int d = depth[n];
-  tokens[i] = d == 0 ? root[b] : topk_ids[(static_cast<long>(b) * K + (d - 1)) * topk + rank[n]];
-  pos[i] = prefix_len[b] + d;
+  // the four independent loads go out together, then the one that needs depth and rank; the
+  // root (depth 0) reads head 0's first candidate, an always valid address, and keeps its own
+  // token
+  const int d = depth[n], r = rank[n], rt = root[b], pl = prefix_len[b];
+  const int tk = topk_ids[(static_cast<long>(b) * K + (d > 0 ? d - 1 : 0)) * topk + (d > 0 ? r : 0)];
+  tokens[i] = d == 0 ? rt : tk;
+  pos[i] = pl + d;
 }
 
 hipError_t launch_tree_gather(const int32_t* topk_ids, int K, int topk, const int32_t* root_tokens,
