@@ -556,13 +556,16 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return v;
 }
 
+// D is a template parameter so that a lane's whole K row (D/4 16-byte loads) and every V load
+// of a batch are issued before any is used
+template <int D>
 __global__ __launch_bounds__(64) void tree_attn_f32(const float* __restrict__ q,
                                                     const float* __restrict__ kc,
                                                     const float* __restrict__ vc,
                                                     const int32_t* __restrict__ prefix_len,
                                                     const uint64_t* __restrict__ mask, float* out,
                                                     long lcap, int Hq, int Hkv, int T, int W,
-                                                    int D, float sl2, int Lmax,
+                                                    float sl2, int Lmax,
                                                     const float* __restrict__ rope_cs) {
   __shared__ float s_q[128];
   __shared__ float s_p[64];
@@ -592,23 +595,27 @@ __global__ __launch_bounds__(64) void tree_attn_f32(const float* __restrict__ q,
   const long ncols = static_cast<long>(L) + T;
   for (long c0 = 0; c0 < ncols; c0 += 64) {
     const long j = c0 + lane;
-    bool vis = j < ncols;
-    if (vis && j >= L) {
-      const int t = static_cast<int>(j - L);
-      vis = (mask[static_cast<long>(i) * W + t / 64] >> (t % 64)) & 1ull;
-    }
+    const bool inr = j < ncols;
+    // the mask word and the key row go out together (a column past the range reads the first
+    // word and the first row, always valid); a masked-out tree column is computed and dropped
+    const int t = inr && j >= L ? static_cast<int>(j - L) : 0;
+    const uint64_t mw = mask[static_cast<long>(i) * W + t / 64];
     float s = -INFINITY;
-    if (vis) {
-      const float4* kr = reinterpret_cast<const float4*>(kc + (base + j) * D);
+    const float4* kr = reinterpret_cast<const float4*>(kc + (base + (inr ? j : 0)) * D);
+    float4 kv[D / 4];
+#pragma unroll
+    for (int d4 = 0; d4 < D / 4; ++d4) kv[d4] = kr[d4];
+    const bool vis = inr && (j < L || ((mw >> (t % 64)) & 1ull));
+    {
       float acc = 0.f;
+#pragma unroll
       for (int d4 = 0; d4 < D / 4; ++d4) {
-        const float4 kv = kr[d4];
-        acc = fmaf(s_q[4 * d4], kv.x, acc);
-        acc = fmaf(s_q[4 * d4 + 1], kv.y, acc);
-        acc = fmaf(s_q[4 * d4 + 2], kv.z, acc);
-        acc = fmaf(s_q[4 * d4 + 3], kv.w, acc);
+        acc = fmaf(s_q[4 * d4], kv[d4].x, acc);
+        acc = fmaf(s_q[4 * d4 + 1], kv[d4].y, acc);
+        acc = fmaf(s_q[4 * d4 + 2], kv[d4].z, acc);
+        acc = fmaf(s_q[4 * d4 + 3], kv[d4].w, acc);
       }
-      s = acc * sl2;
+      if (vis) s = acc * sl2;
     }
     const float mnew = fmaxf(m, wave_max_f32(s));
     const float muse = mnew == -INFINITY ? 0.f : mnew;
@@ -698,10 +705,15 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
   const float sl2 = scale * 1.4426950408889634f;
   if (dtype == 0) {
     hook_before(K_ATTENTION, s);
-    tree_attn_f32<<<static_cast<unsigned>(static_cast<long>(B) * Hq * T), 64, 0, s>>>(
-        static_cast<const float*>(q), static_cast<const float*>(kc), static_cast<const float*>(vc),
-        prefix_len, mask, static_cast<float*>(out), lcap, Hq, Hkv, T, W, D, sl2, max_prefix_len,
-        rope_cs);
+    const unsigned g = static_cast<unsigned>(static_cast<long>(B) * Hq * T);
+    if (D == 128)
+      tree_attn_f32<128><<<g, 64, 0, s>>>(
+          static_cast<const float*>(q), static_cast<const float*>(kc), static_cast<const float*>(vc),
+          prefix_len, mask, static_cast<float*>(out), lcap, Hq, Hkv, T, W, sl2, max_prefix_len, rope_cs);
+    else
+      tree_attn_f32<64><<<g, 64, 0, s>>>(
+          static_cast<const float*>(q), static_cast<const float*>(kc), static_cast<const float*>(vc),
+          prefix_len, mask, static_cast<float*>(out), lcap, Hq, Hkv, T, W, sl2, max_prefix_len, rope_cs);
     hook_after(K_ATTENTION, s);
     return hipGetLastError();
   }
