@@ -380,20 +380,25 @@ __global__ __launch_bounds__(256) void heads_gemv_f32(const float* __restrict__ 
   const int hd = ep.hd, B = ep.B;
   const float* w = W + (static_cast<long>(weight_head(ep, k)) * ep.rows + row) * hd;
   const float* xk = x + static_cast<long>(k) * x_kstride;
+  // lane b < B finishes sequence b's output; its first-layer inputs are loaded up front
+  EpiIn pre{0.f, 0.f};
+  if (ep.mode == 0 && lane < B) pre = epi_inputs(ep, k, row, lane);
   float acc[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) acc[b] = 0.f;
   for (int j = lane * 4; j < hd; j += 256) {
+    // the weight and all 8 vector loads go out together (sequences past B read sequence 0's
+    // vector and are ignored)
     const float4 wv = *reinterpret_cast<const float4*>(w + j);
+    float4 xv[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) xv[b] = *reinterpret_cast<const float4*>(xk + (b < B ? b : 0) * x_bstride + j);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      if (b < B) {
-        const float4 xv = *reinterpret_cast<const float4*>(xk + b * x_bstride + j);
-        acc[b] = fmaf(wv.x, xv.x, acc[b]);
-        acc[b] = fmaf(wv.y, xv.y, acc[b]);
-        acc[b] = fmaf(wv.z, xv.z, acc[b]);
-        acc[b] = fmaf(wv.w, xv.w, acc[b]);
-      }
+      acc[b] = fmaf(wv.x, xv[b].x, acc[b]);
+      acc[b] = fmaf(wv.y, xv[b].y, acc[b]);
+      acc[b] = fmaf(wv.z, xv[b].z, acc[b]);
+      acc[b] = fmaf(wv.w, xv[b].w, acc[b]);
     }
   }
 #pragma unroll
@@ -402,7 +407,7 @@ __global__ __launch_bounds__(256) void heads_gemv_f32(const float* __restrict__ 
       float v = acc[b];
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-      if (lane == b) heads_epilogue(ep, k, row, b, v);
+      if (lane == b) heads_epilogue_in(ep, k, row, b, v, pre);
     }
   }
 }
