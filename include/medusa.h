@@ -39,6 +39,13 @@
  * For measurement only: medusa_set_kernel_events (HIP events around each kernel family) and
  * medusa_stream_read (a plain HBM read, the bandwidth ceiling the heads are compared with).
  *
+ * Tuning overrides, read from the environment once per process (unset: the measured defaults).
+ * They change launch shapes and so the order of fp32 sums, never what is computed:
+ *   MEDUSA_W1_VARIANT, MEDUSA_W2_VARIANT  0..12, the packed bf16 GEMV variant of each layer;
+ *   MEDUSA_ATTN_WG_TARGET                 work-groups tree attention splits K/V to reach (256);
+ *   MEDUSA_ACCEPT_UNROLL                  1, 2, 4 or 8 rounds per acceptance chunk (workspace
+ *                                         sizes follow it, so set it before the first query).
+ *
  * Conventions for every entry point:
  *   - Pointers marked "device" are HIP device memory on the current device; "host" pointers are
  *     ordinary host memory.  Every tensor is dense, row-major, 16-byte aligned.  The caller owns
