@@ -211,17 +211,38 @@ __global__ __launch_bounds__(256) void heads_gemv_bf16(const uint16_t* __restric
 // bf16 weights pre-packed in MFMA fragment order
 // ------------------------------------------------------------------------------------------
 // Packed layout (medusa_pack_weights).  The rows of all K heads are cut into 16-row tiles,
-// numbered gt = k*ntiles + tile (G = K*ntiles tiles in all).  For each 32-column block kb, the
-// 64 lanes' 16-byte A fragments of tile gt sit back to back in 1 KB block number kb*G + gt:
-//   P[kb][k][tile][lane][e] = W[k][16*tile + lane%16][32*kb + 8*(lane/16) + e]   (0 past the rows)
-// One wave-wide 16-byte load reads 1 KB of contiguous memory, and waves working on neighbouring
-// tiles at the same contraction step read neighbouring kilobytes, so the resident waves sweep
-// one contiguous window of the weights together.
+// numbered gt = k*ntiles + tile (G = K*ntiles tiles in all).  The 64 lanes' 16-byte A fragments
+// of tile gt for 32-column block kb form one 1 KB block:
+//   block(gt, kb)[lane][e] = W[k][16*tile + lane%16][32*kb + 8*(lane/16) + e]   (0 past the rows)
+// The tiles are cut into groups of gs consecutive tiles, gs being the tiles that one round of
+// the persistent grid reads (pack_group_tiles); inside group g (of size n, gs but for the last)
+// the blocks are kb-major: block(g*gs + w, kb) is block number g*nkb*gs + kb*n + w.  One
+// wave-wide 16-byte load reads 1 KB of contiguous memory; the waves of a round read neighbouring
+// kilobytes at each contraction step, and each step's window follows the previous one, so the
+// persistent grid sweeps the weights in address order, as a plain read does.
 // Work item = TPW consecutive tiles of one head.  KSPLIT = 4: the 4 waves of a work-group split
 // the contraction of one item and meet in LDS (short matrices: more bytes in flight).
 // KSPLIT = 1: a wave owns an item and its whole contraction; with PERSIST the grid holds about
 // two work-groups per CU and each wave takes items in grid-stride order, which keeps the window
 // that the resident waves read narrow.
+constexpr long kPersistWgs = 512;            // about two work-groups per CU
+
+// Tiles per group of the packed layout: the waves one round of the persistent one-tile-per-wave
+// grid holds (the fewest rounds of 4*kPersistWgs waves, then just enough work-groups for them).
+__host__ __device__ __forceinline__ long pack_group_tiles(long G) {
+  const long rounds = (G + 4 * kPersistWgs - 1) / (4 * kPersistWgs);
+  return 4 * ((G + 4 * rounds - 1) / (4 * rounds));
+}
+// 1 KB block number of (tile gt, contraction block kb), and the distance in blocks from kb to
+// kb + 1 for that tile (its group's size)
+__host__ __device__ __forceinline__ long pack_block(long G, long gs, int nkb, long gt, long kb,
+                                                    long& kbstride_blocks) {
+  const long g = gt / gs, w = gt - g * gs;
+  const long n = G - g * gs < gs ? G - g * gs : gs;
+  kbstride_blocks = n;
+  return g * nkb * gs + kb * n + w;
+}
+
 template <int TPW, int U, int KSPLIT, bool PERSIST>
 __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restrict__ Wp,
                                                           const uint16_t* __restrict__ xsrc,
@@ -237,7 +258,7 @@ __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restr
   const int xph = ep.mode == 1 || ep.x_per_head;
   const int hd = ep.hd;
   const int nkb = hd >> 5;
-  const long kbstride = G * 512;                        // elements from block kb to kb + 1
+  const long gs = pack_group_tiles(G);
   const int kb0 = KSPLIT == 4 ? (wave * nkb) >> 2 : 0;
   const int kb1 = KSPLIT == 4 ? ((wave + 1) * nkb) >> 2 : nkb;
   const int g = lane >> 4, n = lane & 15;
@@ -261,11 +282,15 @@ __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restr
     const int k = static_cast<int>(item / per_head);
     const long t0 = (item - static_cast<long>(k) * per_head) * TPW;
     const uint16_t* ap[TPW];
+    long kbstride[TPW];                                 // elements from block kb to kb + 1
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       long tt = t0 + t;
       if (tt > ntiles - 1) tt = ntiles - 1;             // ragged: valid address, result dropped
-      ap[t] = Wp + (static_cast<long>(weight_head(ep, k)) * ntiles + tt) * 512 + static_cast<long>(kb0) * kbstride + lane * 8;
+      long sb;
+      const long blk = pack_block(G, gs, nkb, static_cast<long>(weight_head(ep, k)) * ntiles + tt, kb0, sb);
+      ap[t] = Wp + blk * 512 + lane * 8;
+      kbstride[t] = sb * 512;
     }
     const uint16_t* xp = n < ncols ? xsrc + (static_cast<long>(k) * ncols * xph + n) * hd + g * 8
                                    : nullptr;
@@ -289,11 +314,11 @@ __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restr
 #pragma unroll
       for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) a[u][t] = load_bf16x8_nt(ap[t] + u * kbstride);
+        for (int t = 0; t < TPW; ++t) a[u][t] = load_bf16x8_nt(ap[t] + u * kbstride[t]);
         x[u] = x_operand(xp, kb + u);
       }
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) ap[t] += U * kbstride;
+      for (int t = 0; t < TPW; ++t) ap[t] += U * kbstride[t];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -304,7 +329,7 @@ __global__ __launch_bounds__(256) void heads_gemv_packed(const uint16_t* __restr
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         a[t] = load_bf16x8_nt(ap[t]);
-        ap[t] += kbstride;
+        ap[t] += kbstride[t];
       }
       const bf16x8_t x = x_operand(xp, kb);
 #pragma unroll
@@ -356,10 +381,16 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __res
   if (i >= total16) return;
   const long ntiles = (rows + 15) >> 4;
   const long G = ntiles * K;
+  const int nkb = hd >> 5;
+  const long gs = pack_group_tiles(G);
   const int lane = static_cast<int>(i & 63);
   const long blk = i >> 6;
-  const long kb = blk / G;
-  const long gt = blk - kb * G;
+  // invert the block number: group, then kb-major inside the group
+  const long g = blk / (static_cast<long>(nkb) * gs);
+  const long off = blk - g * nkb * gs;
+  const long n = G - g * gs < gs ? G - g * gs : gs;
+  const long kb = off / n;
+  const long gt = g * gs + (off - kb * n);
   const long k = gt / ntiles, tile = gt - k * ntiles;
   const long row = tile * 16 + (lane & 15);
   uint4 v = make_uint4(0, 0, 0, 0);
@@ -651,7 +682,6 @@ static const PackedVariant kPackedVariants[] = {
 // non-persistent waves with two tiles sharing each x load.
 constexpr int kDefaultW1Variant = 0;
 static int default_w2_variant(int B) { return B <= 2 ? 10 : (B <= 4 ? 8 : 4); }
-constexpr long kPersistWgs = 512;            // about two work-groups per CU
 
 static int variant_from_env(const char* name, int dflt) {
   const char* v = getenv(name);

@@ -120,17 +120,26 @@ def test_heads_deterministic():
 
 # ---- packed weights (medusa_pack_weights + medusa_heads_packed) ----------------------------
 def _pack_reference(w):
-    """The documented packed order, written out with numpy."""
+    """The documented packed order, written out with numpy: 16-row tiles of all heads in groups
+    of as many tiles as one round of 2048 persistent waves reads, kb-major inside a group."""
     K, rows, hd = w.shape
     nt = (rows + 15) // 16
     padded = np.zeros((K, nt * 16, hd), w.dtype)
     padded[:, :rows] = w
-    # [K][tile][16 rows][hd/32 kb][4 groups][8] -> [kb][K][tile][group][row][8]
-    x = padded.reshape(K, nt, 16, hd // 32, 4, 8).transpose(3, 0, 1, 4, 2, 5)
-    return np.ascontiguousarray(x).reshape(-1)
+    G = K * nt
+    rounds = (G + 2047) // 2048
+    gs = 4 * ((G + 4 * rounds - 1) // (4 * rounds))
+    # [tile][16 rows][hd/32 kb][4 lane groups][8]
+    x = padded.reshape(G, 16, hd // 32, 4, 8)
+    # inside a group: [kb][tile][lane group][row][8]
+    parts = [np.ascontiguousarray(x[g0:g0 + gs].transpose(2, 0, 3, 1, 4)).reshape(-1)
+             for g0 in range(0, G, gs)]
+    return np.concatenate(parts)
 
 
-@pytest.mark.parametrize("K,rows,hd", [(1, 16, 32), (2, 37, 64), (3, 1000, 256), (1, 5, 4096)])
+@pytest.mark.parametrize("K,rows,hd", [(1, 16, 32), (2, 37, 64), (3, 1000, 256), (1, 5, 4096),
+                                       (2, 20000, 64),      # 2500 tiles: groups of 1252 and 1248
+                                       (3, 32000, 32)])     # 6000 tiles: three groups of 2000
 def test_pack_layout(K, rows, hd):
     import torch
     m = lib()
