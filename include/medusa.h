@@ -168,11 +168,16 @@ size_t medusa_packed_weight_bytes(int K, long rows, int hidden);
 /*
  * Packs w (device, [K, rows, hidden] bf16, [out, in]) into `packed` (device,
  * medusa_packed_weight_bytes(K, rows, hidden) bytes).  The rows of all heads are cut into 16-row
- * tiles; for each 32-column block kb, the 64 lanes' 16-byte operands of every tile of every head
- * follow one another (1 KB per tile), rows past `rows` zero-filled:
- *   packed[kb][k][tile][lane][e] = w[k][16 tile + lane % 16][32 kb + 8 (lane / 16) + e],
- * kb < hidden / 32, tile < ceil(rows / 16), lane < 64, e < 8.
- * Done once per model, outside the decode loop.
+ * tiles, numbered gt = k * ntiles + tile (G = K * ntiles, ntiles = ceil(rows / 16)).  The 64
+ * lanes' 16-byte operands of tile gt for 32-column block kb form one 1 KB block, rows past
+ * `rows` zero-filled:
+ *   block(gt, kb)[lane][e] = w[k][16 tile + lane % 16][32 kb + 8 (lane / 16) + e],
+ * kb < hidden / 32, lane < 64, e < 8.  The tiles are grouped gs at a time, with
+ * rounds = ceil(G / 2048) and gs = 4 ceil(G / (4 rounds)) (the tiles one round of the heads
+ * kernel's persistent grid reads); inside group g, of n tiles (gs, or what is left for the
+ * last), the blocks are kb-major: block(g gs + w, kb) is 1 KB block number g nkb gs + kb n + w.
+ * The heads kernels then read the weights in address order.  Done once per model, outside the
+ * decode loop.
  * Limits: 1 <= K <= 64 (K heads, or K * n_blocks stacked block weights for medusa_heads_ex),
  *         1 <= rows < 2^31, hidden a multiple of 32 in 32..16384.
  */
