@@ -41,7 +41,7 @@
  *
  * Tuning overrides, read from the environment once per process (unset: the measured defaults).
  * They change launch shapes and so the order of fp32 sums, never what is computed:
- *   MEDUSA_W1_VARIANT, MEDUSA_W2_VARIANT  0..12, the packed bf16 GEMV variant of each layer;
+ *   MEDUSA_W1_VARIANT, MEDUSA_W2_VARIANT  0..13, the packed bf16 GEMV variant of each layer;
  *   MEDUSA_ATTN_WG_TARGET                 work-groups tree attention splits K/V to reach (256);
  *   MEDUSA_ACCEPT_UNROLL                  1, 2, 4 or 8 rounds per acceptance chunk (workspace
  *                                         sizes follow it, so set it before the first query).

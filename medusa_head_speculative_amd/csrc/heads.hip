@@ -675,17 +675,18 @@ struct PackedVariant {
 static const PackedVariant kPackedVariants[] = {
     {1, 8, 4, 0}, {2, 8, 4, 0}, {1, 8, 1, 0}, {2, 4, 1, 0}, {2, 8, 1, 0}, {4, 4, 1, 0},
     {1, 8, 1, 1}, {1, 16, 1, 1}, {2, 8, 1, 1}, {2, 4, 1, 1}, {1, 4, 1, 1}, {1, 16, 4, 0},
-    {1, 4, 4, 0}};
+    {1, 4, 4, 0}, {8, 1, 1, 0}};
 // Defaults from timing each variant on MI355X at the workload shapes (hidden 4096-8192, vocab
 // 32000-128256): B <= 2 persistent with one tile per wave, B <= 4 persistent with two tiles per
 // wave, B > 4 (16 vector columns, so the x loads cost as much as the weight loads) one grid of
-// non-persistent waves with two tiles sharing each x load.
+// non-persistent waves with eight tiles sharing each x load, one block in flight per tile (on
+// the 33B shape at B = 8: 186.5 us, against 202 us with two tiles per wave and 8 blocks).
 constexpr int kDefaultW1Variant = 0;
-static int default_w2_variant(int B) { return B <= 2 ? 10 : (B <= 4 ? 8 : 4); }
+static int default_w2_variant(int B) { return B <= 2 ? 10 : (B <= 4 ? 8 : 13); }
 
 static int variant_from_env(const char* name, int dflt) {
   const char* v = getenv(name);
-  if (!v) return dflt;
+  if (!v || !*v) return dflt;
   const int i = atoi(v);
   return (i >= 0 && i < static_cast<int>(sizeof(kPackedVariants) / sizeof(kPackedVariants[0]))) ? i : dflt;
 }
@@ -721,6 +722,7 @@ static void launch_packed(int variant, const uint16_t* Wp, const uint16_t* x, in
     MEDUSA_PACKED_CASE(9, 2, 4, 1, true)
     MEDUSA_PACKED_CASE(10, 1, 4, 1, true)
     MEDUSA_PACKED_CASE(11, 1, 16, 4, false)
+    MEDUSA_PACKED_CASE(13, 8, 1, 1, false)
     default: MEDUSA_PACKED_CASE(12, 1, 4, 4, false)
   }
 #undef MEDUSA_PACKED_CASE
