@@ -185,8 +185,11 @@ __global__ __launch_bounds__(512 / NMB, 2) void tree_attn_bf16(AttnArgs a) {
   const int np = (L + kKvTile - 1) / kKvTile;
   const int ntt = (a.T + kKvTile - 1) / kKvTile;
   const int ntiles = np + ntt;
-  const int t_begin = static_cast<int>((static_cast<long>(split) * ntiles) / a.splits);
-  const int t_end = static_cast<int>((static_cast<long>(split + 1) * ntiles) / a.splits);
+  // split s covers tiles [ceil(s n / S), ceil((s + 1) n / S)): the longer splits come first and
+  // the last one, which holds the tree tiles (masked, with the mask scan before them), is the
+  // shortest
+  const int t_begin = static_cast<int>((static_cast<long>(split) * ntiles + a.splits - 1) / a.splits);
+  const int t_end = static_cast<int>((static_cast<long>(split + 1) * ntiles + a.splits - 1) / a.splits);
   const long kvbase = (static_cast<long>(b) * a.Hkv + kvh) * a.lcap;
 
   // ---- tree tiles that some row of this work-group can see (only needed if the K/V range of
