@@ -33,8 +33,9 @@ constexpr int kAccPerThread = 8;
 constexpr int kAccVec = kAccThreads * kAccPerThread;    // elements per load round of a work-group
 constexpr long kPathWideBytes = 32 << 10;   // leaf rows above this size get a 1024-thread block
 constexpr int kMaxTreeTokens = 4096;
-// Rounds of kAccVec elements per work-group of accept_chunks: the largest U of 8, 4, 2 that still
-// leaves at least 1024 work-groups (2048 when there are more than 256 rows), else 1.  Fitted to
+// Rounds of kAccVec elements per work-group of accept_chunks: the larger U of 4, 2 that still
+// leaves at least 1024 work-groups (2048 when there are more than 256 rows), else 1; 8 rounds
+// was never the fastest (70B-layer rows: 58.0 against 54.5 us for 4, three runs each).  Fitted to
 // timings on MI355X once every round's loads were in flight together (event-timed acceptance,
 // U = 1 / 2 / 4 / 8): 7B rows (32) 14.2 / 14.6 / 15.7 / 18.6 us; Llama-8B rows (37 of 128256)
 // 18.5 / 17.0 / 17.6 / 19.7; 33B rows (352 of 32000) 30.2 / 27.4 / 28.5 / 29.3; 70B-layer rows
@@ -44,7 +45,7 @@ static int accept_unroll(int B, long V, int n_int) {
   if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced;
   const long rows = static_cast<long>(n_int) * B;
   const long target = rows <= 256 ? 1024 : 2048;
-  for (int u = 8; u >= 2; u >>= 1) {
+  for (int u = 4; u >= 2; u >>= 1) {
     const long C = (V + static_cast<long>(kAccVec) * u - 1) / (static_cast<long>(kAccVec) * u);
     if (C * rows >= target) return u;
   }
