@@ -26,15 +26,11 @@ largest count; next_token is the argmax of the row of the last accepted node on 
 
 import numpy as np
 
-
-def _bf16_to_f64(bits):
-    return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32) \
-        .astype(np.float64)
+from . import bf16
 
 
 def _row_f64(logits, dtype, b, n):
-    row = logits[b, n]
-    return _bf16_to_f64(row) if dtype == "bf16" else row.astype(np.float64)
+    return bf16.to_f64(logits[b, n], dtype)
 
 
 def _argmax_lowest(x):

@@ -17,14 +17,10 @@ Readings where the pages stop:
 
 import numpy as np
 
+from . import bf16
 from .heads import project
 
-
-def _f64(a, dtype):
-    a = np.asarray(a)
-    if dtype == "bf16" and a.dtype == np.uint16:
-        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    return a.astype(np.float64)
+_f64 = bf16.to_f64
 
 
 def layer_norm(x, gamma, beta, eps):

@@ -17,19 +17,8 @@ Readings where the pages are silent (they never name the encoding):
 
 import numpy as np
 
+from . import bf16
 from .attention import tree_attention
-
-
-def to_bf16(x):
-    """Exact fp64 values -> bf16 bit patterns, round to nearest even (finite, normal range)."""
-    m, e = np.frexp(np.asarray(x, np.float64))       # x = m * 2^e, 0.5 <= |m| < 1
-    r = np.rint(m * 256.0) * np.exp2(e - 8.0)         # 8 significant bits, ties to even
-    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
-
-
-def from_bf16(bits):
-    return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32) \
-        .astype(np.float64)
 
 
 def rope(x, pos, base=10000.0):
@@ -45,11 +34,11 @@ def rope(x, pos, base=10000.0):
 
 
 def _round(x, dtype):
-    return to_bf16(x) if dtype == "bf16" else x.astype(np.float32)
+    return bf16.round_rne(x) if dtype == "bf16" else x.astype(np.float32)
 
 
 def _decode(x, dtype):
-    return from_bf16(x) if dtype == "bf16" else np.asarray(x, np.float64)
+    return bf16.to_f64(x, dtype)
 
 
 def rotate_tree(q, k_cache, dtype, prefix_len, position_ids, base=10000.0):

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle import bf16
 from oracle.rope import rope
 from synth.configs import custom
 from synth.gen import gen_attention_inputs, rng_for
@@ -104,3 +105,17 @@ def test_rotate_tree_touches_only_tree_rows_and_rounds_bf16():
         assert np.array_equal(kr[b, :, L + T:], a["k_cache"][b, :, L + T:])
         # the root (depth 0) turns by prefix_len radians-per-frequency, so it changes unless L = 0
         assert not np.array_equal(kr[b, :, L], a["k_cache"][b, :, L])
+    # the rotated values are rounded once from fp64 to the nearest bf16 (ties to even), which the
+    # pinned rounding of oracle/bf16.py gives; a truncating rounder would differ on many elements
+    q64 = bf16.decode(a["q"])
+    exact = oracle.rope(q64, pos[:, None, :])
+    assert np.array_equal(qr, bf16.round_rne(exact))
+    trunc = (exact.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    assert np.mean(qr != trunc) > 0.2
+    # every rotated value is within half a bf16 step (2^-8 relative) of the exact rotation
+    back = bf16.decode(qr)
+    assert np.all(np.abs(back - exact) <= np.abs(exact) * 2.0 ** -8 + 2.0 ** -133)
+    for b, L in enumerate([9, 2]):
+        rows = bf16.decode(a["k_cache"][b, :, L:L + T])
+        want = bf16.round_rne(oracle.rope(rows, pos[b][None, :]))
+        assert np.array_equal(kr[b, :, L:L + T], want)
