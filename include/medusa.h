@@ -43,7 +43,7 @@
  * They change launch shapes and so the order of fp32 sums, never what is computed:
  *   MEDUSA_W1_VARIANT, MEDUSA_W2_VARIANT  0..13, the packed bf16 GEMV variant of each layer;
  *   MEDUSA_ATTN_WG_TARGET                 work-groups tree attention splits K/V to reach (256);
- *   MEDUSA_ACCEPT_UNROLL                  1, 2, 4 or 8 rounds per acceptance chunk (workspace
+ *   MEDUSA_ACCEPT_UNROLL                  1, 2 or 4 rounds per acceptance chunk (workspace
  *                                         sizes follow it, so set it before the first query).
  *
  * Conventions for every entry point:
@@ -203,6 +203,7 @@ typedef struct {
   int n_paths;     /* root-to-leaf paths (leaves) */
   int dmax;        /* tree depth */
   int n_internal;  /* nodes with at least one child (the root included) */
+  int max_rank;    /* largest rank in the list: build_tree needs topk > max_rank */
   /* device arrays, filled by build_tree(static_ready = 0) */
   uint64_t* mask;      /* [T][W]: bit j%64 of word j/64 of row i is set iff node j is i or an
                           ancestor of i (Wiblog page, tree-attention section: each token sees
@@ -218,8 +219,8 @@ typedef struct {
 } medusa_tree;
 
 /*
- * Host only.  Validates a choice list and fills T, W, n_paths, dmax and n_internal of *tree
- * (its pointers are left untouched).  Returns MEDUSA_ERR_TREE for a malformed list.
+ * Host only.  Validates a choice list and fills T, W, n_paths, dmax, n_internal and max_rank of
+ * *tree (its pointers are left untouched).  Returns MEDUSA_ERR_TREE for a malformed list.
  * Limits: 1 <= n_choices, T <= 4096, 1 <= max_depth <= K <= 8, 1 <= topk <= 64.
  */
 int medusa_tree_dims(const int32_t* choices, int n_choices, int max_depth, int K, int topk,
@@ -234,7 +235,9 @@ int medusa_tree_dims(const int32_t* choices, int n_choices, int max_depth, int K
  * static_ready == 0: the choice list (host) is validated, the static arrays of *tree are
  *   computed on the host and copied into its device arrays (sized from medusa_tree_dims); the
  *   host waits for that copy.  Do this once per tree; the pages precompute and cache the mask.
- * static_ready == 1: the device arrays are taken as already filled; choices may be NULL.
+ * static_ready == 1: the device arrays are taken as already filled; choices may be NULL.  The
+ *   dims in *tree must still fit this call: dmax <= K and max_rank < topk (else
+ *   MEDUSA_ERR_TREE), since the gather reads topk_ids[b][depth - 1][rank].
  * Arguments: topk_ids device [B][K][topk]; root_tokens, prefix_len device [B];
  *            tokens, position_ids device [B][T] int32.
  */

@@ -28,7 +28,7 @@ class MedusaError(RuntimeError):
 
 class medusa_tree(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int), ("W", ctypes.c_int), ("n_paths", ctypes.c_int),
-                ("dmax", ctypes.c_int), ("n_internal", ctypes.c_int),
+                ("dmax", ctypes.c_int), ("n_internal", ctypes.c_int), ("max_rank", ctypes.c_int),
                 ("mask", ctypes.c_void_p), ("parent", ctypes.c_void_p),
                 ("depth", ctypes.c_void_p), ("rank", ctypes.c_void_p),
                 ("paths", ctypes.c_void_p), ("path_len", ctypes.c_void_p),
@@ -236,7 +236,8 @@ class Tree:
     @property
     def dims(self):
         c = self.c
-        return dict(T=c.T, W=c.W, n_paths=c.n_paths, dmax=c.dmax, n_internal=c.n_internal)
+        return dict(T=c.T, W=c.W, n_paths=c.n_paths, dmax=c.dmax, n_internal=c.n_internal,
+                    max_rank=c.max_rank)
 
 
 def build_tree(tree, topk_ids, root_tokens, prefix_len, tokens, position_ids, stream=None):

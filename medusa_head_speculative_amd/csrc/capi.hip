@@ -43,7 +43,7 @@ bool dtype_ok(int dt) { return dt == MEDUSA_F32 || dt == MEDUSA_BF16; }
 
 // ---- static tree (host) -------------------------------------------------------------------
 struct HostTree {
-  int T = 0, W = 0, P = 0, dmax = 0, n_int = 0;
+  int T = 0, W = 0, P = 0, dmax = 0, n_int = 0, max_rank = 0;
   std::vector<uint64_t> mask;
   std::vector<int32_t> parent, depth, rank, paths, path_len, child_ptr, child_idx, internal;
 };
@@ -96,6 +96,7 @@ int parse_tree(const int32_t* choices, int n, int max_depth, int K, int topk, Ho
   h.P = 0;
   h.n_int = 0;
   for (int i = 0; i < T; ++i) (nchild[i] == 0 ? h.P : h.n_int) += 1;
+  h.max_rank = *std::max_element(rank.begin(), rank.end());
   if (!want_arrays) return MEDUSA_OK;
   h.parent = parent;
   h.depth = depth;
@@ -255,6 +256,7 @@ int medusa_tree_dims(const int32_t* choices, int n_choices, int max_depth, int K
   tree->n_paths = h.P;
   tree->dmax = h.dmax;
   tree->n_internal = h.n_int;
+  tree->max_rank = h.max_rank;
   g_err[0] = '\0';
   return MEDUSA_OK;
 }
@@ -275,7 +277,7 @@ int build_tree(const int32_t* choices, int n_choices, int max_depth, int K, int 
     HostTree h;
     if ((rc = parse_tree(choices, n_choices, max_depth, K, topk, &h, true))) return rc;
     if (tree->T != h.T || tree->W != h.W || tree->n_paths != h.P || tree->dmax != h.dmax ||
-        tree->n_internal != h.n_int)
+        tree->n_internal != h.n_int || tree->max_rank != h.max_rank)
       return fail(MEDUSA_ERR_TREE, "tree dims do not match the choice list (call medusa_tree_dims)");
     if ((rc = check_pending())) return rc;
     if ((rc = upload(tree->mask, h.mask, "mask")) || (rc = upload(tree->parent, h.parent, "parent")) ||
@@ -288,6 +290,11 @@ int build_tree(const int32_t* choices, int n_choices, int max_depth, int K, int 
       return rc;
   } else {
     if (tree->T < 2 || tree->T > 4096) return fail(MEDUSA_ERR_TREE, "tree->T = %d", tree->T);
+    // the gather reads topk_ids[b][depth - 1][rank]: the tree must fit this K and topk
+    if (tree->dmax < 1 || tree->dmax > K)
+      return fail(MEDUSA_ERR_TREE, "tree->dmax = %d does not fit K = %d", tree->dmax, K);
+    if (tree->max_rank < 0 || tree->max_rank >= topk)
+      return fail(MEDUSA_ERR_TREE, "tree->max_rank = %d does not fit topk = %d", tree->max_rank, topk);
     if ((rc = check_pending())) return rc;
   }
   return launched(medusa::launch_tree_gather(topk_ids, K, topk, root_tokens, prefix_len, B, tree->T,
@@ -396,11 +403,12 @@ size_t typical_accept_workspace(int B, int T, long vocab, int n_internal) {
   return medusa::accept_ws_layout(B, T, vocab, n_internal).total;
 }
 
-int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
-                   const int32_t* tokens, const medusa_tree* tree, float temperature,
-                   float posterior_threshold, float posterior_alpha, int32_t* best_candidate,
-                   int32_t* accept_length, int32_t* next_token, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+// Checks of typical_accept's arguments other than the workspace; *need receives the workspace
+// bytes the call takes.
+static int accept_args(const void* logits, int dtype, int B, int T, long vocab,
+                       const int32_t* tokens, const medusa_tree* tree, float temperature,
+                       float posterior_threshold, float posterior_alpha,
+                       const int32_t* best_candidate, const int32_t* accept_length, size_t* need) {
   if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_DTYPE, "dtype = %d", dtype);
   if (!logits || !tokens || !tree || !best_candidate || !accept_length)
     return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
@@ -416,19 +424,40 @@ int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
     return fail(MEDUSA_ERR_ARG, "posterior_threshold = %g, need 0 < eps < 1", posterior_threshold);
   if (!(posterior_alpha > 0.f) || !std::isfinite(posterior_alpha))
     return fail(MEDUSA_ERR_ARG, "posterior_alpha = %g, need > 0", posterior_alpha);
-  const size_t need = medusa::accept_ws_layout(B, T, vocab, tree->n_internal).total;
-  if (!workspace || workspace_bytes < need)
-    return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  *need = medusa::accept_ws_layout(B, T, vocab, tree->n_internal).total;
+  return MEDUSA_OK;
+}
+
+static int accept_launch(const void* logits, int dtype, int B, int T, long vocab,
+                         const int32_t* tokens, const medusa_tree* tree, float temperature,
+                         float posterior_threshold, float posterior_alpha, int32_t* best_candidate,
+                         int32_t* accept_length, int32_t* next_token, char* ws, void* stream,
+                         const char* what) {
   int rc;
   if ((rc = check_pending())) return rc;
   return launched(medusa::launch_typical_accept(logits, dtype, B, T, vocab, tokens, tree->n_internal,
                                                 tree->internal, tree->child_ptr, tree->child_idx,
                                                 tree->paths, tree->path_len, tree->n_paths, tree->dmax,
                                                 temperature, posterior_threshold, posterior_alpha,
-                                                best_candidate, accept_length, next_token,
-                                                static_cast<char*>(workspace),
+                                                best_candidate, accept_length, next_token, ws,
                                                 static_cast<hipStream_t>(stream)),
-                  "typical_accept");
+                  what);
+}
+
+int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
+                   const int32_t* tokens, const medusa_tree* tree, float temperature,
+                   float posterior_threshold, float posterior_alpha, int32_t* best_candidate,
+                   int32_t* accept_length, int32_t* next_token, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  int rc = accept_args(logits, dtype, B, T, vocab, tokens, tree, temperature, posterior_threshold,
+                       posterior_alpha, best_candidate, accept_length, &need);
+  if (rc) return rc;
+  if (!workspace || workspace_bytes < need)
+    return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  return accept_launch(logits, dtype, B, T, vocab, tokens, tree, temperature, posterior_threshold,
+                       posterior_alpha, best_candidate, accept_length, next_token,
+                       static_cast<char*>(workspace), stream, "typical_accept");
 }
 
 // ---- commit of the accepted candidate --------------------------------------------------------

@@ -13,8 +13,8 @@
 // handoff is a kernel boundary):
 //   accept_chunks  one work-group per (sequence, internal row, chunk) computes in a single pass
 //                  the chunk's max y, S = sum 2^(y - max) and A = sum (y - max) 2^(y - max) with
-//                  y = l * log2(e) / T, plus the argmax (a chunk is 1 to 8 rounds of 8 elements
-//                  per thread, see accept_unroll);
+//                  y = l * log2(e) / T, plus the argmax (a chunk is 1, 2 or 4 rounds of 8
+//                  elements per thread, see accept_unroll);
 //   accept_rows    one work-group per (sequence, internal row) merges the row's partials in chunk
 //                  order, so H = ln2 * (log2 S - A / S) and ln p(x) = ln2 * (y_x - max - log2 S),
 //                  and decides the row's children in the log domain;
@@ -39,10 +39,10 @@ constexpr int kMaxTreeTokens = 4096;
 // timings on MI355X once every round's loads were in flight together (event-timed acceptance,
 // U = 1 / 2 / 4 / 8): 7B rows (32) 14.2 / 14.6 / 15.7 / 18.6 us; Llama-8B rows (37 of 128256)
 // 18.5 / 17.0 / 17.6 / 19.7; 33B rows (352 of 32000) 30.2 / 27.4 / 28.5 / 29.3; 70B-layer rows
-// (444 of 128256) 75 / 56.6 / 54.4 / 57.6.  MEDUSA_ACCEPT_UNROLL = 1, 2, 4 or 8 overrides it.
+// (444 of 128256) 75 / 56.6 / 54.4 / 57.6.  MEDUSA_ACCEPT_UNROLL = 1, 2 or 4 overrides it.
 static int accept_unroll(int B, long V, int n_int) {
   static const int forced = [] { const char* v = getenv("MEDUSA_ACCEPT_UNROLL"); return v ? atoi(v) : 0; }();
-  if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced;
+  if (forced == 1 || forced == 2 || forced == 4) return forced;
   const long rows = static_cast<long>(n_int) * B;
   const long target = rows <= 256 ? 1024 : 2048;
   for (int u = 4; u >= 2; u >>= 1) {
@@ -542,8 +542,7 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, lo
   const int load = vec ? (dtype == 1 ? 1 : 2) : 0;
   const bool wide = V * (dtype == 1 ? 2 : 4) > kPathWideBytes;
 #define MEDUSA_ACCEPT_LAUNCH(LD)                                                    \
-  if (L.unroll == 8) accept_chunks<8, LD><<<grid, kAccThreads, 0, s>>>(a);        \
-  else if (L.unroll == 4) accept_chunks<4, LD><<<grid, kAccThreads, 0, s>>>(a);   \
+  if (L.unroll == 4) accept_chunks<4, LD><<<grid, kAccThreads, 0, s>>>(a);        \
   else if (L.unroll == 2) accept_chunks<2, LD><<<grid, kAccThreads, 0, s>>>(a);   \
   else accept_chunks<1, LD><<<grid, kAccThreads, 0, s>>>(a);                      \
   accept_rows<<<dim3(n_internal, B), kAccThreads, 0, s>>>(a);                      \

@@ -64,6 +64,7 @@ def test_tree_dims_match_the_oracle(m):
         assert rc == 0
         assert (t.T, t.W, t.n_paths, t.dmax) == (st["T"], st["W"], len(st["paths"]), st["dmax"])
         assert t.n_internal == sum(1 for c in st["children"] if c)
+        assert t.max_rank == max(max(c) for c in ch)
 
 
 @pytest.mark.parametrize("ch,K,topk", [
@@ -101,8 +102,19 @@ def test_invalid_arguments_fail_before_any_launch(m):
     assert "workspace" in L.medusa_last_error().decode()
     assert L.tree_attention(p, p, p, 1, p, 10, 5, p, 1, 4, 4, 9, 64, 0.0, p, p, 1 << 20, None) == -2
     assert L.tree_attention(p, p, p, 1, p, 10, 100, p, 1, 4, 3, 9, 64, 0.0, p, p, 1 << 20, None) == -2
-    t = m._lib.medusa_tree(T=9, W=1, n_paths=6, dmax=2, n_internal=3, mask=16, parent=16, depth=16,
-                           rank=16, paths=16, path_len=16, child_ptr=16, child_idx=16, internal=16)
+    t = m._lib.medusa_tree(T=9, W=1, n_paths=6, dmax=2, n_internal=3, max_rank=2, mask=16,
+                           parent=16, depth=16, rank=16, paths=16, path_len=16, child_ptr=16,
+                           child_idx=16, internal=16)
+    # build_tree on an uploaded tree (static_ready = 1): the gather reads
+    # topk_ids[b][depth - 1][rank], so a K below the tree's depth or a topk not above its largest
+    # rank is rejected before any launch
+    def bt(K, topk, ready):
+        return L.build_tree(None, 0, 0, K, topk, p, p, p, 1, ready, ctypes.byref(t), p, p, None)
+    assert bt(1, 3, 1) == -4                       # K = 1 < dmax = 2
+    assert "dmax" in L.medusa_last_error().decode()
+    assert bt(2, 2, 1) == -4                       # topk = 2 <= max_rank = 2
+    assert "max_rank" in L.medusa_last_error().decode()
+    assert bt(2, 3, 2) == -1                       # static_ready must be 0 or 1
     args = [p, 1, 1, 9, 100, p, ctypes.byref(t)]
     outs = [p, p, p, p, 1 << 20, None]
     assert L.typical_accept(*args, -1.0, 0.09, 0.3, *outs) == -1

@@ -77,8 +77,8 @@ def test_accept_full_size(ci, temp):
     (1, "one", 1, 0.7), (7, "c0", 2, 0.7), (2047, "c1", 3, 1.0), (2049, "c1", 3, 0.0),
     (5000, "chain6", 2, 0.7), (4100, "c3", 5, 0.3), (300, "c2", 8, 3.0),
     (20001, "c4", 5, 0.7),      # 555 rows: 2 rounds per chunk, element loads (V % 8 != 0)
-    (131072, "chain8", 16, 0.7),   # 128 rows: 8 rounds per chunk, vector loads
-    (131077, "chain8", 16, 0.0),   # 8 rounds per chunk, element loads, ragged last chunk
+    (131072, "chain8", 16, 0.7),   # 128 rows: 4 rounds per chunk, vector loads
+    (131077, "chain8", 16, 0.0),   # 4 rounds per chunk, element loads, ragged last chunk
 ])
 def test_accept_edges(dtype, V, tree, B, temp):
     m = lib()
