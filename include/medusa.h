@@ -326,6 +326,27 @@ int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
                    int32_t* accept_length, int32_t* next_token, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/*
+ * typical_accept for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation, arguments and
+ * results, without the workspace.  The intermediates go to a scratch array that the library
+ * holds in device memory, one copy of MEDUSA_NOALLOC_SCRATCH_BYTES per GPU it runs on, kept
+ * until the process ends.  The call allocates nothing and frees nothing; the first call on a
+ * device looks up that device's copy (hipGetSymbolAddress).  Every call on one GPU shares its
+ * copy: calls that overlap in time on one GPU (on different streams, or from different host
+ * threads) race and must be serialised by the caller.  The scratch needs no clearing: each call
+ * writes every intermediate before reading it.
+ * Errors: those of typical_accept, and MEDUSA_ERR_WORKSPACE when typical_accept_workspace(B, T,
+ * vocab, tree->n_internal) exceeds MEDUSA_NOALLOC_SCRATCH_BYTES (8 MiB holds, for example,
+ * B = 64 sequences of a 1111-node tree with 111 internal rows at vocab 128256).
+ */
+#define MEDUSA_NOALLOC_SCRATCH_BYTES (8 << 20)
+int typical_accept_noalloc(const void* logits, int dtype, int B, int T, long vocab,
+                           const int32_t* tokens, const medusa_tree* tree, float temperature,
+                           float posterior_threshold, float posterior_alpha,
+                           int32_t* best_candidate, int32_t* accept_length, int32_t* next_token,
+                           void* stream);
+
 /* ---------------------------------------------------------------------------------------- *
  * 5. Commit of the accepted candidate (decode-loop glue)
  * ---------------------------------------------------------------------------------------- */

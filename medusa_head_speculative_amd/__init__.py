@@ -29,6 +29,7 @@ from ._lib import (  # noqa: F401
     tree_attention_rope_workspace,
     tree_attention_workspace,
     typical_accept,
+    typical_accept_noalloc,
     typical_accept_workspace,
     workspace,
 )

@@ -42,7 +42,7 @@ EXPORTS = ["medusa_last_error", "medusa_heads_workspace", "medusa_heads", "medus
            "medusa_heads_packed", "medusa_packed_weight_bytes", "medusa_pack_weights",
            "medusa_stream_read", "commit_accepted", "tree_attention_rope_workspace",
            "tree_attention_rope", "medusa_sparse_tree", "medusa_heads_ex_workspace",
-           "medusa_heads_ex"]
+           "medusa_heads_ex", "typical_accept_noalloc"]
 
 KERNELS = ["heads_w1", "heads_w2", "topk", "tree_gather", "attention", "attn_combine", "accept",
            "commit", "rope"]
@@ -79,6 +79,8 @@ def load():
     L.typical_accept_workspace.argtypes = [i, i, l, i]
     L.typical_accept.restype = i
     L.typical_accept.argtypes = [vp, i, i, i, l, vp, tp, f, f, f, vp, vp, vp, vp, sz, vp]
+    L.typical_accept_noalloc.restype = i
+    L.typical_accept_noalloc.argtypes = [vp, i, i, i, l, vp, tp, f, f, f, vp, vp, vp, vp]
     L.medusa_set_kernel_events.restype = i
     L.medusa_heads_packed.restype = i
     L.medusa_heads_packed.argtypes = [vp, vp, vp, vp, i, i, l, i, i, vp, vp, vp, vp, sz, vp]
@@ -294,6 +296,18 @@ def typical_accept(logits, tokens, tree, temperature, posterior_threshold, poste
                                  ctypes.byref(tree.c), temperature, posterior_threshold,
                                  posterior_alpha, _ptr(best_candidate), _ptr(accept_length),
                                  _ptr(next_token), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def typical_accept_noalloc(logits, tokens, tree, temperature, posterior_threshold,
+                           posterior_alpha, best_candidate, accept_length, next_token=None,
+                           stream=None):
+    """typical_accept without a workspace: the library's per-GPU scratch array holds the
+    intermediates (for callers that cannot allocate; overlapping calls on one GPU race)."""
+    B, T, V = logits.shape
+    _check(load().typical_accept_noalloc(_ptr(logits), dtype_code(logits), B, T, V, _ptr(tokens),
+                                         ctypes.byref(tree.c), temperature, posterior_threshold,
+                                         posterior_alpha, _ptr(best_candidate),
+                                         _ptr(accept_length), _ptr(next_token), _stream(stream)))
 
 
 def commit_accepted(tree, best_candidate, accept_length, tokens, next_token, k_cache, v_cache,

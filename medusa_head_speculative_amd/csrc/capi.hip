@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <vector>
 
 #include "../../include/medusa.h"
@@ -458,6 +459,58 @@ int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
   return accept_launch(logits, dtype, B, T, vocab, tokens, tree, temperature, posterior_threshold,
                        posterior_alpha, best_candidate, accept_length, next_token,
                        static_cast<char*>(workspace), stream, "typical_accept");
+}
+
+// ---- typical acceptance without a caller workspace --------------------------------------------
+// Its intermediates live in `scratch`, a device array of the library (one copy per GPU, held
+// until the process ends).  In host code the array's name is only a stand-in for the symbol: the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MEDUSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up on its first use.
+int scratch_address(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MEDUSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MEDUSA_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MEDUSA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return MEDUSA_OK;
+}
+}  // namespace
+
+int typical_accept_noalloc(const void* logits, int dtype, int B, int T, long vocab,
+                           const int32_t* tokens, const medusa_tree* tree, float temperature,
+                           float posterior_threshold, float posterior_alpha,
+                           int32_t* best_candidate, int32_t* accept_length, int32_t* next_token,
+                           void* stream) {
+  size_t need = 0;
+  int rc = accept_args(logits, dtype, B, T, vocab, tokens, tree, temperature, posterior_threshold,
+                       posterior_alpha, best_candidate, accept_length, &need);
+  if (rc) return rc;
+  if (need > MEDUSA_NOALLOC_SCRATCH_BYTES)
+    return fail(MEDUSA_ERR_WORKSPACE,
+                "typical_accept_noalloc: these sizes need %zu bytes of scratch, more than the %d "
+                "bytes the library holds per GPU (use typical_accept with a workspace)",
+                need, MEDUSA_NOALLOC_SCRATCH_BYTES);
+  char* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return accept_launch(logits, dtype, B, T, vocab, tokens, tree, temperature, posterior_threshold,
+                       posterior_alpha, best_candidate, accept_length, next_token, ws, stream,
+                       "typical_accept_noalloc");
 }
 
 // ---- commit of the accepted candidate --------------------------------------------------------

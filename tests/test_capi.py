@@ -122,6 +122,13 @@ def test_invalid_arguments_fail_before_any_launch(m):
     assert L.typical_accept(*args, 0.7, 0.09, 0.0, *outs) == -1
     assert L.typical_accept(p, 1, 1, 8, 100, p, ctypes.byref(t), 0.7, 0.09, 0.3, *outs) == -2
     assert L.typical_accept(*args, 0.7, 0.09, 0.3, p, p, p, p, 8, None) == -5
+    # the allocation-free variant: the same checks, then a request larger than the library's
+    # per-GPU scratch (8 MiB) is refused before anything touches the GPU
+    assert L.typical_accept_noalloc(*args, -1.0, 0.09, 0.3, p, p, p, None) == -1
+    assert L.typical_accept_noalloc(p, 1, 4000, 9, 1 << 20, p, ctypes.byref(t), 0.7, 0.09, 0.3,
+                                    p, p, p, None) == -5
+    assert "scratch" in L.medusa_last_error().decode()
+    assert L.typical_accept_workspace(4000, 9, 1 << 20, 3) > 8 << 20
     ca = [ctypes.byref(t), 2, p, p, p, p, p, p]                 # tree .. v_cache
     rest = [p, p, p, p, p, None, 0, None, None]                   # prefix .. stream
     assert L.commit_accepted(*ca, 7, 4, 64, 128, *rest) == -3
