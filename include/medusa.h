@@ -115,7 +115,7 @@ size_t medusa_heads_workspace(int B, int hidden, long vocab, int K, int topk);
  *   topk_logits [B, K, topk] float32, or NULL
  * Arithmetic: fp32 accumulation; r is kept in fp32.  For bf16 weights the fp32 r enters the
  * matrix cores as a bf16 hi + lo pair (relative error about 2^-17 per element).
- * Limits: 1 <= B <= 8, 32 <= hidden <= 16384 and hidden % 32 == 0, 1 <= vocab < 2^31,
+ * Limits: 1 <= B <= 8, 8 <= hidden <= 16384 and hidden % 8 == 0, 1 <= vocab < 2^31,
  *         1 <= K <= 8, 1 <= topk <= min(64, vocab).
  */
 int medusa_heads(const void* h, const void* w1, const void* b1, const void* w2, int dtype, int B,
@@ -129,6 +129,8 @@ int medusa_heads(const void* h, const void* w1, const void* b1, const void* w2, 
  * medusa_heads with dtype = MEDUSA_BF16; only w1_packed / w2_packed differ:
  *   w1_packed  medusa_packed_weight_bytes(K, hidden, hidden) bytes from w1
  *   w2_packed  medusa_packed_weight_bytes(K, vocab, hidden) bytes from w2
+ * The packed order cuts the hidden dimension into whole 32-column blocks, so a hidden size that
+ * is a multiple of 8 but not of 32 gives MEDUSA_ERR_UNSUPPORTED (medusa_heads serves it).
  */
 int medusa_heads_packed(const void* h, const void* w1_packed, const void* b1,
                         const void* w2_packed, int B, int hidden, long vocab, int K, int topk,
@@ -151,7 +153,8 @@ int medusa_heads_packed(const void* h, const void* w1_packed, const void* b1,
  *   w2     [K][vocab][hidden] dtype, or its packed form (packed = 1)
  * Everything else as medusa_heads; n_blocks = 1 without LayerNorm is exactly medusa_heads
  * (packed = 0) or medusa_heads_packed (packed = 1).  The workspace query takes layernorm = 0/1.
- * Limits: those of medusa_heads, 1 <= n_blocks <= 8, ln_eps > 0.
+ * Limits: those of medusa_heads (packed = 1: those of medusa_heads_packed), 1 <= n_blocks <= 8,
+ * ln_eps > 0.
  */
 size_t medusa_heads_ex_workspace(int B, int hidden, long vocab, int K, int n_blocks, int layernorm,
                                  int topk);

@@ -149,10 +149,14 @@ extern "C" {
 const char* medusa_last_error(void) { return g_err; }
 
 // ---- heads ----------------------------------------------------------------------------------
-static int heads_shape(int B, int hidden, long vocab, int K, int topk) {
+// packed: the weights come in the matrix-core operand order of medusa_pack_weights, which cuts
+// the hidden dimension into whole 32-column blocks
+static int heads_shape(int B, int hidden, long vocab, int K, int topk, bool packed = false) {
   if (B < 1 || B > 8) return fail(MEDUSA_ERR_SHAPE, "B = %d, need 1..8", B);
-  if (hidden < 32 || hidden > 16384 || hidden % 32)
-    return fail(MEDUSA_ERR_SHAPE, "hidden = %d, need a multiple of 32 in 32..16384", hidden);
+  if (hidden < 8 || hidden > 16384 || hidden % 8)
+    return fail(MEDUSA_ERR_SHAPE, "hidden = %d, need a multiple of 8 in 8..16384", hidden);
+  if (packed && hidden % 32)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "hidden = %d: packed weights need a multiple of 32", hidden);
   if (vocab < 1 || vocab >= (1l << 31)) return fail(MEDUSA_ERR_SHAPE, "vocab = %ld out of range", vocab);
   if (K < 1 || K > 8) return fail(MEDUSA_ERR_SHAPE, "K = %d, need 1..8", K);
   if (topk < 1 || topk > 64 || topk > vocab) return fail(MEDUSA_ERR_SHAPE, "topk = %d, need 1..min(64, vocab)", topk);
@@ -198,7 +202,7 @@ int medusa_heads_ex(const void* h, const void* w1, const void* b1, const void* l
   if ((ln_gamma == nullptr) != (ln_beta == nullptr))
     return fail(MEDUSA_ERR_ARG, "give both ln_gamma and ln_beta or neither");
   if (ln_gamma && !(ln_eps > 0.f && std::isfinite(ln_eps))) return fail(MEDUSA_ERR_ARG, "ln_eps = %g, need > 0", ln_eps);
-  int rc = heads_shape(B, hidden, vocab, K, topk);
+  int rc = heads_shape(B, hidden, vocab, K, topk, packed != 0);
   if (rc) return rc;
   if (n_blocks < 1 || n_blocks > 8) return fail(MEDUSA_ERR_SHAPE, "n_blocks = %d, need 1..8", n_blocks);
   const size_t need = medusa::heads_ws_layout(B, hidden, vocab, K, topk, n_blocks, ln_gamma ? 1 : 0).total;
@@ -233,7 +237,7 @@ int medusa_heads_packed(const void* h, const void* w1_packed, const void* b1,
                         float* logits, int32_t* topk_ids, float* topk_logits, void* workspace,
                         size_t workspace_bytes, void* stream) {
   if (!h || !w1_packed || !b1 || !w2_packed || !topk_ids) return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
-  int rc = heads_shape(B, hidden, vocab, K, topk);
+  int rc = heads_shape(B, hidden, vocab, K, topk, true);
   if (rc) return rc;
   const size_t need = medusa::heads_ws_layout(B, hidden, vocab, K, topk).total;
   if (!workspace || workspace_bytes < need)

@@ -144,8 +144,11 @@ __global__ __launch_bounds__(256) void heads_gemv_bf16(const uint16_t* __restric
   const int k = blockIdx.y;
   const long row0 = static_cast<long>(blockIdx.x) * (16 * TPW);
   const int hd = ep.hd;
-  const int nkb = hd >> 5;
+  // 32-column contraction blocks; when hd % 32 != 0 (hd is a multiple of 8) the last block is
+  // partial and the wave that owns it loads zeros for its columns past hd
+  const int nkb = (hd + 31) >> 5, nfull = hd >> 5;
   const int kb0 = (wave * nkb) >> 2, kb1 = ((wave + 1) * nkb) >> 2;
+  const int kb1f = kb1 < nfull ? kb1 : nfull;
   const int g = lane >> 4, n = lane & 15;
 
   const uint16_t* wrow[TPW];
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(256) void heads_gemv_bf16(const uint16_t* __restric
   for (int t = 0; t < TPW; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   int kb = kb0;
-  for (; kb + 4 <= kb1; kb += 4) {
+  for (; kb + 4 <= kb1f; kb += 4) {
     bf16x8_t a[4][TPW], x[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -177,11 +180,23 @@ __global__ __launch_bounds__(256) void heads_gemv_bf16(const uint16_t* __restric
 #pragma unroll
       for (int t = 0; t < TPW; ++t) acc[t] = mfma16x16x32(a[u][t], x[u], acc[t]);
   }
-  for (; kb < kb1; ++kb) {
+  for (; kb < kb1f; ++kb) {
     bf16x8_t a[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) a[t] = load_bf16x8_nt(wrow[t] + kb * 32);
     const bf16x8_t x = x_operand(xp, kb);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) acc[t] = mfma16x16x32(a[t], x, acc[t]);
+  }
+  if (kb1 > nfull) {
+    // the partial last block: columns kb*32 + 8g .. +7 exist only when below hd (a multiple of
+    // 8, so a lane's 8 columns are all in the row or all past it); the others contribute zeros
+    // and are never loaded
+    const bool in = nfull * 32 + g * 8 < hd;
+    bf16x8_t a[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) a[t] = in ? load_bf16x8_nt(wrow[t] + nfull * 32) : zero_bf16x8();
+    const bf16x8_t x = in ? x_operand(xp, nfull) : zero_bf16x8();
 #pragma unroll
     for (int t = 0; t < TPW; ++t) acc[t] = mfma16x16x32(a[t], x, acc[t]);
   }

@@ -82,7 +82,9 @@ def test_tree_dims_rejects_malformed_lists(m, ch, K, topk):
 def test_workspace_queries(m):
     assert m.medusa_heads_workspace(1, 4096, 32000, 4, 10) > 4 * 32000 * 4
     assert m.medusa_heads_workspace(9, 4096, 32000, 4, 10) == 0      # B > 8
-    assert m.medusa_heads_workspace(1, 4016, 32000, 4, 10) == 0      # hidden % 32
+    assert m.medusa_heads_workspace(1, 4012, 32000, 4, 10) == 0      # hidden % 8
+    assert m.medusa_heads_workspace(1, 4, 32000, 4, 10) == 0         # hidden < 8
+    assert m.medusa_heads_workspace(1, 264, 32000, 4, 10) > 0        # any multiple of 8
     assert m.medusa_heads_workspace(1, 4096, 32000, 4, 65) == 0      # topk > 64
     assert m.tree_attention_workspace(1, 32, 32, 65, 128, 1024) > 0
     assert m.tree_attention_workspace(1, 32, 5, 65, 128, 1024) == 0  # Hq % Hkv
@@ -100,6 +102,12 @@ def test_invalid_arguments_fail_before_any_launch(m):
     assert L.medusa_heads(p, p, p, p, 1, 1, 64, 100, 9, 1, None, p, None, p, 1 << 20, None) == -2
     assert L.medusa_heads(p, p, p, p, 1, 1, 64, 100, 1, 1, None, p, None, p, 16, None) == -5
     assert "workspace" in L.medusa_last_error().decode()
+    # hidden a multiple of 8 but not of 32: the plain heads take it, the packed order cannot
+    assert L.medusa_heads(p, p, p, p, 1, 1, 264, 100, 1, 1, None, p, None, p, 16, None) == -5
+    assert L.medusa_heads_packed(p, p, p, p, 1, 264, 100, 1, 1, None, p, None, p, 1 << 20, None) == -7
+    assert L.medusa_heads_ex(p, p, p, None, None, 1e-5, p, 1, 1, 1, 264, 100, 1, 1, 1, None, p, None,
+                             p, 1 << 20, None) == -7
+    assert L.medusa_packed_weight_bytes(1, 100, 264) == 0
     assert L.tree_attention(p, p, p, 1, p, 10, 5, p, 1, 4, 4, 9, 64, 0.0, p, p, 1 << 20, None) == -2
     assert L.tree_attention(p, p, p, 1, p, 10, 100, p, 1, 4, 3, 9, 64, 0.0, p, p, 1 << 20, None) == -2
     t = m._lib.medusa_tree(T=9, W=1, n_paths=6, dmax=2, n_internal=3, max_rank=2, mask=16,

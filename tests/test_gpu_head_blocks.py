@@ -49,6 +49,8 @@ def _run(m, h, w1, b1, w2, g, be, dtype, packed, V, K, nb, topk):
     ("f32", False, 2, False, 2, 256, 1000, 3),
     ("f32", False, 3, True, 1, 256, 777, 2),
     ("bf16", False, 2, True, 3, 512, 3000, 2),
+    ("bf16", False, 2, True, 2, 264, 1000, 3),      # hidden a multiple of 8, not of 32
+    ("f32", False, 2, True, 3, 8, 50, 2),
     ("bf16", True, 3, False, 1, 1024, 5000, 3),
     ("bf16", True, 2, True, 8, 512, 2000, 2),
     ("bf16", True, 2, True, 1, 4096, 32000, 4),     # the Vicuna-7B head shape with 2 LN blocks
