@@ -55,6 +55,17 @@ def tol(dtype):
     return 1e-4 if dtype == "f32" else 2e-2
 
 
+def sample_units(B, Hq, T, n, seed):
+    """(b, q head, node) units at which a full-size attention output is compared with the
+    oracle: every head of the first and the last sequence at a few nodes (the last sequence's
+    units are the ones a work plan runs last), plus n random units."""
+    from synth.gen import rng_for
+    rng = rng_for(seed, 9)
+    sel = [(b, h, i) for b in {0, B - 1} for h in range(Hq) for i in {0, 1, T // 2, T - 1}]
+    sel += [(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(T))) for _ in range(n)]
+    return np.array(sorted(set(sel)), np.int32)
+
+
 def mask_array(static):
     return np.array(static["mask"], dtype=np.uint64)
 

@@ -152,3 +152,33 @@ def test_accept_strict_parameters_and_determinism():
     _compare(st, res, logits, "bf16", got)
     got2 = run_accept(m, tr, logits, tokens, 0.7, 0.12, 0.35)
     assert all(np.array_equal(x, y) for x, y in zip(got, got2))
+
+
+SWEEP = [(0, 0.7, 16), (1, 0.0, 16), (1, 0.7, 16), (2, 0.0, 16), (2, 0.7, 16), (3, 0.7, 4),
+         (4, 0.0, 4), (4, 0.7, 4)]
+
+
+@pytest.mark.parametrize("ci,temp,nseeds", SWEEP)
+def test_accept_seed_sweep(ci, temp, nseeds):
+    """Every workload shape over several seeds (16 on the three smaller, 4 on the two largest):
+    fresh tree tokens and verification logits per seed.  Decisions inside the 1e-4 band may go
+    either way; their number is bounded (at most 1 in 500 of the decisions, and at least 2)."""
+    cfg = get_config(ci)
+    m = lib()
+    choices = load_tree_choices(f"c{ci}")
+    banded = decisions = 0
+    lens = []
+    for j in range(nseeds):
+        seed = 100 + j
+        st, tree, tokens = _tree_and_tokens(m, choices, cfg.K, cfg.topk, cfg.B, cfg.V, seed=seed)
+        logits = gen_verif_logits(cfg, st["parent"], tokens, seed=seed)
+        res = oracle.typical_accept(logits, cfg.dtype, tokens, st, float(np.float32(temp)),
+                                    float(np.float32(0.09)), float(np.float32(0.3)))
+        say("accept seed sweep", cfg.name, temp, seed)
+        got = run_accept(m, tree, logits, tokens, temp)
+        banded += _compare(st, res, logits, cfg.dtype, got)
+        decisions += cfg.B * (st["T"] - 1)
+        lens += got[1].tolist()
+    print(f"{cfg.name} T={temp}: {nseeds} seeds, accept lengths {lens}, "
+          f"banded {banded} of {decisions} decisions")
+    assert banded <= max(2, decisions // 500)

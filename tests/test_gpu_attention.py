@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import as_f64, dev, host, lib, mask_array, say, tol
+from gpu_util import as_f64, dev, host, lib, mask_array, sample_units, say, tol
 from synth import gen_attention_inputs, get_config
 from synth.configs import custom
 from synth.gen import rng_for
@@ -27,12 +27,7 @@ def run_attn(m, a, mask, Hkv, max_pl=None):
 
 
 def _sample_units(B, Hq, T, n, seed):
-    rng = rng_for(seed, 9)
-    # every head of the first and the last sequence at a few nodes (the last sequence's units are
-    # the ones the work plan runs last, cut into K/V splits), plus random rows
-    sel = [(b, h, i) for b in {0, B - 1} for h in range(Hq) for i in {0, 1, T // 2, T - 1}]
-    sel += [(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(T))) for _ in range(n)]
-    return np.array(sorted(set(sel)), np.int32)
+    return sample_units(B, Hq, T, n, seed)
 
 
 @pytest.mark.parametrize("ci", [0, 1, 2, 3, 4])
