@@ -58,3 +58,12 @@ def check_input(a, dtype):
     assert a.dtype == want, (a.dtype, dtype)
     assert a.flags.c_contiguous
     return a
+
+
+def set_threads(n):
+    """Threads the OpenMP loops of the C part use from now on (for timing the oracle; its results
+    do not depend on it: every sum keeps its order).  Returns the count now in force."""
+    L = lib()
+    L.omp_set_num_threads(int(n))
+    L.omp_get_max_threads.restype = ctypes.c_int
+    return int(L.omp_get_max_threads())
