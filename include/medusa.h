@@ -330,6 +330,39 @@ int typical_accept(const void* logits, int dtype, int B, int T, long vocab,
                    size_t workspace_bytes, void* stream);
 
 /*
+ * The candidate-filtering call as the cnnetsun page writes it (candidate-filtering section):
+ *     evaluate_posterior(logits, candidates, temperature, posterior_threshold, posterior_alpha,
+ *                        top_p, sampling, fast) -> (best_candidate, accept_length).
+ * The page names top_p, sampling and fast and defines none of them; they are read as follows.
+ *   sampling  which test a candidate passes at temperature > 0:
+ *     MEDUSA_SAMPLING_TYPICAL  the typical-acceptance test of typical_accept (top_p unused);
+ *                              with it this call is exactly typical_accept;
+ *     MEDUSA_SAMPLING_NUCLEUS  child c of node n is accepted iff it lies in the top_p nucleus of
+ *                              p = softmax(logits[b][n] / temperature): the probability mass of
+ *                              the tokens whose logit is strictly larger than tokens[b][c]'s is
+ *                              below top_p (tokens tied with it are not counted, so tied tokens
+ *                              are in or out together).  Decided in fp32 from a single pass over
+ *                              the row (sums of 2^(y - max) in a fixed order).
+ *   At temperature 0 both modes are greedy (Wiblog page, typical-acceptance section).
+ *   top_p     0 < top_p <= 1 (1: every candidate with a finite logit is in the nucleus).
+ *   fast      0 or 1: a faster evaluation of the same rule.  This library has one evaluation,
+ *             the single pass over each internal row, so the results do not depend on it.
+ * Everything else (arguments, outputs, the path scan, next_token, errors) as typical_accept.
+ * The workspace query takes the tree's dims (T, n_internal) and the mode; the nucleus mode
+ * keeps 64 per-child partial sums for every chunk of every internal row on top of
+ * typical_accept's workspace.  Errors: MEDUSA_ERR_ARG for a sampling, fast or top_p outside
+ * the values above.
+ */
+typedef enum { MEDUSA_SAMPLING_TYPICAL = 0, MEDUSA_SAMPLING_NUCLEUS = 1 } medusa_sampling;
+size_t evaluate_posterior_workspace(int B, long vocab, const medusa_tree* tree, int sampling);
+int evaluate_posterior(const void* logits, int dtype, int B, int T, long vocab,
+                       const int32_t* tokens, const medusa_tree* tree, float temperature,
+                       float posterior_threshold, float posterior_alpha, float top_p,
+                       int sampling, int fast, int32_t* best_candidate, int32_t* accept_length,
+                       int32_t* next_token, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * typical_accept for callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the same computation, arguments and
  * results, without the workspace.  The intermediates go to a scratch array that the library

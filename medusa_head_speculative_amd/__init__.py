@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     Tree,
     build_tree,
     commit_accepted,
+    evaluate_posterior,
+    evaluate_posterior_workspace,
     load,
     medusa_heads,
     medusa_heads_ex,

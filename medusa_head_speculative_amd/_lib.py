@@ -42,7 +42,10 @@ EXPORTS = ["medusa_last_error", "medusa_heads_workspace", "medusa_heads", "medus
            "medusa_heads_packed", "medusa_packed_weight_bytes", "medusa_pack_weights",
            "medusa_stream_read", "commit_accepted", "tree_attention_rope_workspace",
            "tree_attention_rope", "medusa_sparse_tree", "medusa_heads_ex_workspace",
-           "medusa_heads_ex", "typical_accept_noalloc"]
+           "medusa_heads_ex", "typical_accept_noalloc", "evaluate_posterior_workspace",
+           "evaluate_posterior"]
+
+SAMPLING = {"typical": 0, "nucleus": 1}
 
 KERNELS = ["heads_w1", "heads_w2", "topk", "tree_gather", "attention", "attn_combine", "accept",
            "commit", "rope"]
@@ -79,6 +82,11 @@ def load():
     L.typical_accept_workspace.argtypes = [i, i, l, i]
     L.typical_accept.restype = i
     L.typical_accept.argtypes = [vp, i, i, i, l, vp, tp, f, f, f, vp, vp, vp, vp, sz, vp]
+    L.evaluate_posterior_workspace.restype = sz
+    L.evaluate_posterior_workspace.argtypes = [i, l, tp, i]
+    L.evaluate_posterior.restype = i
+    L.evaluate_posterior.argtypes = [vp, i, i, i, l, vp, tp, f, f, f, f, i, i, vp, vp, vp, vp, sz,
+                                     vp]
     L.typical_accept_noalloc.restype = i
     L.typical_accept_noalloc.argtypes = [vp, i, i, i, l, vp, tp, f, f, f, vp, vp, vp, vp]
     L.medusa_set_kernel_events.restype = i
@@ -296,6 +304,23 @@ def typical_accept(logits, tokens, tree, temperature, posterior_threshold, poste
                                  ctypes.byref(tree.c), temperature, posterior_threshold,
                                  posterior_alpha, _ptr(best_candidate), _ptr(accept_length),
                                  _ptr(next_token), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def evaluate_posterior_workspace(B, vocab, tree, sampling="typical"):
+    return load().evaluate_posterior_workspace(B, vocab, ctypes.byref(tree.c), SAMPLING[sampling])
+
+
+def evaluate_posterior(logits, tokens, tree, temperature, posterior_threshold, posterior_alpha,
+                       best_candidate, accept_length, ws, top_p=1.0, sampling="typical",
+                       fast=False, next_token=None, stream=None):
+    """typical_accept with the page's top_p / sampling / fast arguments ("typical" or
+    "nucleus"; see include/medusa.h for their readings)."""
+    B, T, V = logits.shape
+    _check(load().evaluate_posterior(_ptr(logits), dtype_code(logits), B, T, V, _ptr(tokens),
+                                     ctypes.byref(tree.c), temperature, posterior_threshold,
+                                     posterior_alpha, top_p, SAMPLING[sampling], 1 if fast else 0,
+                                     _ptr(best_candidate), _ptr(accept_length), _ptr(next_token),
+                                     _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def typical_accept_noalloc(logits, tokens, tree, temperature, posterior_threshold,

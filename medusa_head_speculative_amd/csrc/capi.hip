@@ -408,12 +408,17 @@ size_t typical_accept_workspace(int B, int T, long vocab, int n_internal) {
   return medusa::accept_ws_layout(B, T, vocab, n_internal).total;
 }
 
-// Checks of typical_accept's arguments other than the workspace; *need receives the workspace
-// bytes the call takes.
+// Children per node at most: siblings carry distinct ranks below topk <= 64.  The nucleus mode
+// keeps one mass per possible child of every chunk.
+constexpr int kMaxChildren = 64;
+
+// Checks of typical_accept's (evaluate_posterior's) arguments other than the workspace; *need
+// receives the workspace bytes the call takes.
 static int accept_args(const void* logits, int dtype, int B, int T, long vocab,
                        const int32_t* tokens, const medusa_tree* tree, float temperature,
                        float posterior_threshold, float posterior_alpha,
-                       const int32_t* best_candidate, const int32_t* accept_length, size_t* need) {
+                       const int32_t* best_candidate, const int32_t* accept_length, size_t* need,
+                       bool nucleus = false) {
   if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_DTYPE, "dtype = %d", dtype);
   if (!logits || !tokens || !tree || !best_candidate || !accept_length)
     return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
@@ -429,7 +434,7 @@ static int accept_args(const void* logits, int dtype, int B, int T, long vocab,
     return fail(MEDUSA_ERR_ARG, "posterior_threshold = %g, need 0 < eps < 1", posterior_threshold);
   if (!(posterior_alpha > 0.f) || !std::isfinite(posterior_alpha))
     return fail(MEDUSA_ERR_ARG, "posterior_alpha = %g, need > 0", posterior_alpha);
-  *need = medusa::accept_ws_layout(B, T, vocab, tree->n_internal).total;
+  *need = medusa::accept_ws_layout(B, T, vocab, tree->n_internal, nucleus ? kMaxChildren : 0).total;
   return MEDUSA_OK;
 }
 
@@ -437,16 +442,55 @@ static int accept_launch(const void* logits, int dtype, int B, int T, long vocab
                          const int32_t* tokens, const medusa_tree* tree, float temperature,
                          float posterior_threshold, float posterior_alpha, int32_t* best_candidate,
                          int32_t* accept_length, int32_t* next_token, char* ws, void* stream,
-                         const char* what) {
+                         const char* what, bool nucleus = false, float top_p = 1.f) {
   int rc;
   if ((rc = check_pending())) return rc;
   return launched(medusa::launch_typical_accept(logits, dtype, B, T, vocab, tokens, tree->n_internal,
                                                 tree->internal, tree->child_ptr, tree->child_idx,
                                                 tree->paths, tree->path_len, tree->n_paths, tree->dmax,
                                                 temperature, posterior_threshold, posterior_alpha,
+                                                nucleus ? 1 : 0, top_p, kMaxChildren,
                                                 best_candidate, accept_length, next_token, ws,
                                                 static_cast<hipStream_t>(stream)),
                   what);
+}
+
+// ---- the candidate-filtering call with its sampling modes ----------------------------------
+static int posterior_mode(float top_p, int sampling, int fast) {
+  if (sampling != MEDUSA_SAMPLING_TYPICAL && sampling != MEDUSA_SAMPLING_NUCLEUS)
+    return fail(MEDUSA_ERR_ARG, "sampling = %d, need MEDUSA_SAMPLING_TYPICAL or _NUCLEUS", sampling);
+  if (fast != 0 && fast != 1) return fail(MEDUSA_ERR_ARG, "fast = %d, need 0 or 1", fast);
+  if (!(top_p > 0.f && top_p <= 1.f)) return fail(MEDUSA_ERR_ARG, "top_p = %g, need 0 < top_p <= 1", top_p);
+  return MEDUSA_OK;
+}
+
+size_t evaluate_posterior_workspace(int B, long vocab, const medusa_tree* tree, int sampling) {
+  if (!tree || (sampling != MEDUSA_SAMPLING_TYPICAL && sampling != MEDUSA_SAMPLING_NUCLEUS)) return 0;
+  const int T = tree->T, n_int = tree->n_internal;
+  if (B < 1 || B > 65535 || T < 2 || T > 4096 || vocab < 1 || vocab >= (1l << 31) || n_int < 1 || n_int >= T)
+    return 0;
+  return medusa::accept_ws_layout(B, T, vocab, n_int,
+                                  sampling == MEDUSA_SAMPLING_NUCLEUS ? kMaxChildren : 0).total;
+}
+
+int evaluate_posterior(const void* logits, int dtype, int B, int T, long vocab,
+                       const int32_t* tokens, const medusa_tree* tree, float temperature,
+                       float posterior_threshold, float posterior_alpha, float top_p,
+                       int sampling, int fast, int32_t* best_candidate, int32_t* accept_length,
+                       int32_t* next_token, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int rc = posterior_mode(top_p, sampling, fast);
+  if (rc) return rc;
+  const bool nucleus = sampling == MEDUSA_SAMPLING_NUCLEUS;
+  size_t need = 0;
+  rc = accept_args(logits, dtype, B, T, vocab, tokens, tree, temperature, posterior_threshold,
+                   posterior_alpha, best_candidate, accept_length, &need, nucleus);
+  if (rc) return rc;
+  if (!workspace || workspace_bytes < need)
+    return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  return accept_launch(logits, dtype, B, T, vocab, tokens, tree, temperature, posterior_threshold,
+                       posterior_alpha, best_candidate, accept_length, next_token,
+                       static_cast<char*>(workspace), stream, "evaluate_posterior", nucleus, top_p);
 }
 
 int typical_accept(const void* logits, int dtype, int B, int T, long vocab,

@@ -64,15 +64,17 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
 
 // ---- typical acceptance ------------------------------------------------------------------
 struct AcceptWs {
-  size_t part, dec, total;
+  size_t part, dec, mass, total;
   int chunks, unroll;
 };
-AcceptWs accept_ws_layout(int B, int T, long V, int n_internal);
+// maxc_nucleus > 0: the nucleus mode's per-child masses for nodes of at most that many children
+AcceptWs accept_ws_layout(int B, int T, long V, int n_internal, int maxc_nucleus = 0);
 hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, long V,
                                  const int32_t* tokens, int n_internal, const int32_t* internal,
                                  const int32_t* child_ptr, const int32_t* child_idx,
                                  const int32_t* paths, const int32_t* path_len, int n_paths,
                                  int dmax, float temperature, float eps, float delta,
+                                 int nucleus, float top_p, int maxc,
                                  int32_t* best, int32_t* accept_len, int32_t* next_token,
                                  char* ws, hipStream_t s);
 

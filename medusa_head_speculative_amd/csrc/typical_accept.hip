@@ -186,8 +186,12 @@ struct AcceptArgs {
   float y_scale;      // log2(e) / temperature
   float ln_eps, ln_delta;
   int C;
+  int nucleus;            // nucleus test in place of the typical one (temperature > 0)
+  float top_p;
+  int maxc;               // children per node at most (nucleus mode)
   RowStat* part_stat;     // [B][n_int][C]
   uint64_t* part_arg;     // [B][n_int][C]
+  float* part_mass;       // [B][n_int][C][maxc] masses above each child (nucleus mode)
   int32_t* dec;           // [B][T]
   int32_t* rowarg;        // [B][T]
   int32_t* best;
@@ -307,6 +311,106 @@ __global__ __launch_bounds__(kAccThreads) void accept_chunks(AcceptArgs a) {
   }
 }
 
+// Kernel 1 of the nucleus mode (temperature > 0), grid (C, n_int, B): the chunk's statistics and
+// argmax as accept_chunks, and for every child j of the row the chunk's sum of 2^(y - m) over
+// the elements whose logit is strictly larger than the child's own: the probability mass above
+// the child, in the units of S.  Every thread takes the block's largest logit as m, so all the
+// per-thread sums share one reference and add without rescaling.
+constexpr int kNucGroup = 16;   // children summed per pass (a node has at most 64)
+template <int U, int LOAD>
+__global__ __launch_bounds__(kAccThreads) void accept_chunks_nucleus(AcceptArgs a) {
+  __shared__ RowStat s_stat[kAccThreads / 64];
+  __shared__ uint64_t s_arg[kAccThreads / 64];
+  __shared__ float s_cl[64];
+  __shared__ float s_max[kAccThreads / 64];
+  __shared__ float s_mass[kAccThreads / 64][kNucGroup];
+  const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const int n = a.internal[r];
+  const int esz = a.dtype == 1 ? 2 : 4;
+  const char* row = static_cast<const char*>(a.logits) + (static_cast<long>(b) * a.T + n) * a.V * esz;
+  const long base = static_cast<long>(c) * kAccVec * U + static_cast<long>(threadIdx.x) * kAccPerThread;
+  float x[U][kAccPerThread];
+  bool valid[U][kAccPerThread];
+  load_rounds<LOAD, U>(row, a.dtype, base, kAccVec, a.V, x, valid);
+  // the children's own logits (+inf for a token outside the vocab: nothing lies above it, and
+  // the decision rejects such a child anyway)
+  // (siblings carry distinct ranks below topk <= 64, so a valid tree never reaches the clamp)
+  const int c0 = a.child_ptr[n], nchild = min(min(a.child_ptr[n + 1] - c0, a.maxc), 64);
+  if (static_cast<int>(threadIdx.x) < nchild) {
+    const int tok = a.tokens[static_cast<long>(b) * a.T + a.child_idx[c0 + threadIdx.x]];
+    s_cl[threadIdx.x] = tok < 0 || tok >= a.V ? INFINITY
+                        : a.dtype == 1 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[tok])
+                                       : reinterpret_cast<const float*>(row)[tok];
+  }
+  uint64_t arg = 0;
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < kAccPerThread; ++e)
+      if (valid[u][e]) {
+        const uint64_t k = sel_key(x[u][e], static_cast<uint32_t>(base + u * kAccVec + e));
+        arg = k > arg ? k : arg;
+        tmax = fmaxf(tmax, x[u][e]);
+      }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off));
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = tmax;
+  __syncthreads();                                     // also publishes s_cl
+  const float xb = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  RowStat st{-INFINITY, 0.f, 0.f, 0.f};
+  float p[U][kAccPerThread];
+  const float m = xb > -INFINITY ? xb * a.y_scale : 0.f;
+  {
+    float S = 0.f, A = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < kAccPerThread; ++e) {
+        const float d = fmaxf(fmaf(x[u][e], a.y_scale, -m), -256.f);
+        p[u][e] = valid[u][e] && xb > -INFINITY ? __builtin_amdgcn_exp2f(d) : 0.f;
+        S += p[u][e];
+        A = fmaf(d, p[u][e], A);
+      }
+    if (xb > -INFINITY) st = RowStat{m, S, A, 0.f};
+  }
+  const long pidx = (static_cast<long>(b) * a.n_int + r) * a.C + c;
+  const int w = threadIdx.x >> 6;
+  for (int g0 = 0; g0 < nchild; g0 += kNucGroup) {
+    float cl[kNucGroup], acc[kNucGroup];
+#pragma unroll
+    for (int j = 0; j < kNucGroup; ++j) {
+      cl[j] = g0 + j < nchild ? s_cl[g0 + j] : INFINITY;
+      acc[j] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < kAccPerThread; ++e)
+#pragma unroll
+        for (int j = 0; j < kNucGroup; ++j) acc[j] += x[u][e] > cl[j] ? p[u][e] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kNucGroup; ++j) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) acc[j] += __shfl_xor(acc[j], off);
+    }
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int j = 0; j < kNucGroup; ++j) s_mass[w][j] = acc[j];
+    }
+    __syncthreads();
+    const int j = threadIdx.x;
+    if (j < kNucGroup && g0 + j < nchild)
+      a.part_mass[pidx * a.maxc + g0 + j] = (s_mass[0][j] + s_mass[1][j]) + (s_mass[2][j] + s_mass[3][j]);
+    __syncthreads();
+  }
+  block_merge(st, arg, false, s_stat, s_arg);
+  if (threadIdx.x == 0) {
+    a.part_stat[pidx] = st;
+    a.part_arg[pidx] = arg;
+  }
+}
+
 // argmax (lowest index on ties) of one row by a block of NT threads, UR rounds of 8 elements
 // per thread in flight.  Each thread keeps its best value and index with float compares in
 // increasing index order (the first maximum wins; -0 == +0) and keys them once at the end; a
@@ -394,6 +498,17 @@ __global__ __launch_bounds__(kAccThreads) void accept_rows(AcceptArgs a) {
       acc = 0;                               // not a vocab id: never accepted, never read
     } else if (a.greedy) {
       acc = static_cast<uint32_t>(tok) == sel_key_index(s_rowarg);
+    } else if (a.nucleus && static_cast<int>(threadIdx.x) >= a.maxc) {
+      acc = 0;                               // more children than a valid tree has (see above)
+    } else if (a.nucleus) {
+      // the mass strictly above the child, merged over the chunks in chunk order, against
+      // top_p of the row's total (both in the units of 2^(y - row max))
+      float mass = 0.f;
+      for (int i = 0; i < a.C; ++i) {
+        const RowStat ps = a.part_stat[prow + i];
+        if (ps.S > 0.f) mass += a.part_mass[(prow + i) * a.maxc + threadIdx.x] * exp2f(ps.m - s_row.m);
+      }
+      acc = mass < a.top_p * s_row.S;
     } else {
       const float log2S = log2f(s_row.S);
       const float ln2 = 0.69314718055994531f;
@@ -485,7 +600,7 @@ __global__ __launch_bounds__(NT) void accept_paths(AcceptArgs a) {
   }
 }
 
-AcceptWs accept_ws_layout(int B, int T, long V, int n_internal) {
+AcceptWs accept_ws_layout(int B, int T, long V, int n_internal, int maxc_nucleus) {
   AcceptWs w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
@@ -495,6 +610,8 @@ AcceptWs accept_ws_layout(int B, int T, long V, int n_internal) {
   w.chunks = static_cast<int>(C);
   w.part = take((sizeof(RowStat) + sizeof(uint64_t)) * static_cast<size_t>(B) * n_internal * C);
   w.dec = take(sizeof(int32_t) * static_cast<size_t>(B) * T * 2);   // decisions + row argmax
+  // nucleus mode: the mass above every child of every chunk
+  w.mass = maxc_nucleus > 0 ? take(sizeof(float) * static_cast<size_t>(B) * n_internal * C * maxc_nucleus) : 0;
   w.total = off;
   return w;
 }
@@ -504,9 +621,10 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, lo
                                  const int32_t* child_ptr, const int32_t* child_idx,
                                  const int32_t* paths, const int32_t* path_len, int n_paths,
                                  int dmax, float temperature, float eps, float delta,
+                                 int nucleus, float top_p, int maxc,
                                  int32_t* best, int32_t* accept_len, int32_t* next_token,
                                  char* ws, hipStream_t s) {
-  const AcceptWs L = accept_ws_layout(B, T, V, n_internal);
+  const AcceptWs L = accept_ws_layout(B, T, V, n_internal, nucleus ? maxc : 0);
   const size_t nstat = static_cast<size_t>(B) * n_internal * L.chunks;
   AcceptArgs a{};
   a.logits = logits;
@@ -528,6 +646,10 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, lo
   a.ln_eps = logf(eps);
   a.ln_delta = logf(delta);
   a.C = L.chunks;
+  a.nucleus = nucleus && !a.greedy;
+  a.top_p = top_p;
+  a.maxc = maxc;
+  a.part_mass = nucleus ? reinterpret_cast<float*>(ws + L.mass) : nullptr;
   a.part_stat = reinterpret_cast<RowStat*>(ws + L.part);
   a.part_arg = reinterpret_cast<uint64_t*>(ws + L.part + sizeof(RowStat) * nstat);
   a.dec = reinterpret_cast<int32_t*>(ws + L.dec);
@@ -541,10 +663,14 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int B, int T, lo
   const bool vec = V % 8 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
   const int load = vec ? (dtype == 1 ? 1 : 2) : 0;
   const bool wide = V * (dtype == 1 ? 2 : 4) > kPathWideBytes;
-#define MEDUSA_ACCEPT_LAUNCH(LD)                                                    \
-  if (L.unroll == 4) accept_chunks<4, LD><<<grid, kAccThreads, 0, s>>>(a);        \
-  else if (L.unroll == 2) accept_chunks<2, LD><<<grid, kAccThreads, 0, s>>>(a);   \
-  else accept_chunks<1, LD><<<grid, kAccThreads, 0, s>>>(a);                      \
+#define MEDUSA_ACCEPT_LAUNCH(LD)                                                             \
+  if (a.nucleus) {                                                                         \
+    if (L.unroll == 4) accept_chunks_nucleus<4, LD><<<grid, kAccThreads, 0, s>>>(a);       \
+    else if (L.unroll == 2) accept_chunks_nucleus<2, LD><<<grid, kAccThreads, 0, s>>>(a);  \
+    else accept_chunks_nucleus<1, LD><<<grid, kAccThreads, 0, s>>>(a);                     \
+  } else if (L.unroll == 4) accept_chunks<4, LD><<<grid, kAccThreads, 0, s>>>(a);          \
+  else if (L.unroll == 2) accept_chunks<2, LD><<<grid, kAccThreads, 0, s>>>(a);            \
+  else accept_chunks<1, LD><<<grid, kAccThreads, 0, s>>>(a);                               \
   accept_rows<<<dim3(n_internal, B), kAccThreads, 0, s>>>(a);                      \
   if (wide) accept_paths<1024, LD><<<B, 1024, 0, s>>>(a);                          \
   else accept_paths<256, LD><<<B, 256, 0, s>>>(a);

@@ -11,7 +11,7 @@ the cache (commit.py).
 """
 
 from . import _clib  # noqa: F401
-from .accept import row_threshold, typical_accept  # noqa: F401
+from .accept import evaluate_posterior, row_threshold, typical_accept  # noqa: F401
 from .attention import tree_attention  # noqa: F401
 from .commit import commit  # noqa: F401
 from .head_blocks import heads_blocks  # noqa: F401

@@ -63,10 +63,40 @@ def scan_paths(static, accepted_b):
     return best, lens[best], paths[best][lens[best]]
 
 
+def softmax(z_row):
+    e = np.exp(z_row - z_row.max())
+    return e / e.sum()
+
+
+def mass_above(p, row, x):
+    """Probability mass, under p (the row's softmax), of the tokens whose logit is strictly
+    larger than token x's (row holds the logits)."""
+    return float(p[row > row[x]].sum())
+
+
 def typical_accept(logits, dtype, tokens, static, temperature, eps=0.09, delta=0.3):
     """logits [B,T,V] (stored dtype), tokens [B][T].  Returns a dict with best_candidate,
     accept_length, next_token (all [B]) plus per-child diagnostics:
       accepted [B,T] bool (root True), margin [B,T] = ln p(tok) - ln thr (nan at T=0 / root)."""
+    return evaluate_posterior(logits, dtype, tokens, static, temperature, eps, delta)
+
+
+def evaluate_posterior(logits, dtype, tokens, static, temperature, eps=0.09, delta=0.3,
+                       top_p=1.0, sampling="typical", fast=False):
+    """The candidate-filtering call of the cnnetsun page, evaluate_posterior(logits, candidates,
+    temperature, posterior_threshold, posterior_alpha, top_p, sampling, fast), under these
+    readings (the page names the last three arguments and defines none of them):
+      sampling = "typical"  the typical-acceptance test above (top_p unused);
+      sampling = "nucleus"  at temperature > 0, child c of node n is accepted iff it lies in the
+                            top_p nucleus of p = softmax(l_n / T): the mass of the tokens whose
+                            logit is strictly larger than tok(c)'s is below top_p
+                            (margin = ln top_p - ln mass, +inf when the mass is 0);
+      temperature 0         greedy in both modes;
+      fast                  a faster evaluation of the same rule: no effect on the result.
+    Returns the dict of typical_accept."""
+    assert sampling in ("typical", "nucleus")
+    assert 0.0 < top_p <= 1.0
+    del fast
     B, T, V = logits.shape
     parent, children = static["parent"], static["children"]
     paths, path_len = static["paths"], static["path_len"]
@@ -85,6 +115,12 @@ def typical_accept(logits, dtype, tokens, static, temperature, eps=0.09, delta=0
             if temperature == 0:
                 for c in children[n]:
                     accepted[b, c] = tokens[b][c] == argmax[b, n]
+            elif sampling == "nucleus":
+                p = softmax(row / temperature)
+                for c in children[n]:
+                    a = mass_above(p, row, tokens[b][c])
+                    accepted[b, c] = a < top_p
+                    margin[b, c] = np.log(top_p) - (np.log(a) if a > 0 else -np.inf)
             else:
                 p, H, thr = row_threshold(row / temperature, eps, delta)
                 H_all[b, n], thr_all[b, n] = H, thr

@@ -130,6 +130,19 @@ def test_invalid_arguments_fail_before_any_launch(m):
     assert L.typical_accept(*args, 0.7, 0.09, 0.0, *outs) == -1
     assert L.typical_accept(p, 1, 1, 8, 100, p, ctypes.byref(t), 0.7, 0.09, 0.3, *outs) == -2
     assert L.typical_accept(*args, 0.7, 0.09, 0.3, p, p, p, p, 8, None) == -5
+    # evaluate_posterior: the page's sampling / fast / top_p arguments are checked first
+    ep = [p, 1, 1, 9, 100, p, ctypes.byref(t), 0.7, 0.09, 0.3]
+    eo = [p, p, p, p, 1 << 20, None]
+    assert L.evaluate_posterior(*ep, 0.9, 2, 0, *eo) == -1          # unknown sampling mode
+    assert L.evaluate_posterior(*ep, 0.9, 1, 2, *eo) == -1          # fast is 0 or 1
+    assert L.evaluate_posterior(*ep, 0.0, 1, 0, *eo) == -1          # top_p in (0, 1]
+    assert L.evaluate_posterior(*ep, 1.5, 0, 0, *eo) == -1
+    assert L.evaluate_posterior(*ep, 0.9, 1, 0, p, p, p, p, 8, None) == -5
+    assert L.evaluate_posterior_workspace(1, 100, ctypes.byref(t), 0) == \
+        L.typical_accept_workspace(1, 9, 100, 3)
+    assert L.evaluate_posterior_workspace(1, 100, ctypes.byref(t), 1) > \
+        L.typical_accept_workspace(1, 9, 100, 3)
+    assert L.evaluate_posterior_workspace(1, 100, ctypes.byref(t), 2) == 0
     # the allocation-free variant: the same checks, then a request larger than the library's
     # per-GPU scratch (8 MiB) is refused before anything touches the GPU
     assert L.typical_accept_noalloc(*args, -1.0, 0.09, 0.3, p, p, p, None) == -1

@@ -218,3 +218,104 @@ def test_equality_rejects():
     res = oracle.typical_accept(logits, "f32", [[0, 1, 2]], st, 1.0, eps=0.25, delta=10.0)
     assert res["threshold"][0, 0] == 0.25
     assert not res["accepted"][0, 1:].any()
+
+
+# ---- nucleus mode of evaluate_posterior (reading: candidate in the top_p nucleus of p) ----
+
+def _nucleus_single_row(row, child_tokens, top_p, temperature=1.0):
+    st = _tree_with_root_children(len(child_tokens))
+    T = st["T"]
+    logits = np.zeros((1, T, len(row)), np.float64)
+    logits[0, 0] = row
+    tokens = [[0] + list(child_tokens)]
+    return oracle.evaluate_posterior(logits, "f64", tokens, st, temperature, top_p=top_p,
+                                     sampling="nucleus")
+
+
+def test_nucleus_hand_worked_row():
+    # p = [0.5, 0.25, 0.125, 0.125, 0]: the mass strictly above each token is 0, 0.5, 0.75,
+    # 0.75 (tokens 2 and 3 tie) and 1 (the -inf token)
+    row = _logits_from_probs([0.5, 0.25, 0.125, 0.125], 5)
+    for top_p, want in [(0.49, [1, 0, 0, 0, 0]), (0.51, [1, 1, 0, 0, 0]), (0.74, [1, 1, 0, 0, 0]),
+                        (0.76, [1, 1, 1, 1, 0]), (1.0, [1, 1, 1, 1, 0])]:
+        res = _nucleus_single_row(row, [0, 1, 2, 3, 4], top_p)
+        assert res["accepted"][0, 1:].astype(int).tolist() == want, top_p
+    res = _nucleus_single_row(row, [0, 1, 2, 3, 4], 0.6)
+    assert np.isinf(res["margin"][0, 1]) and res["margin"][0, 1] > 0      # nothing above the max
+    assert abs(res["margin"][0, 2] - (math.log(0.6) - math.log(0.5))) < 1e-12
+    assert abs(res["margin"][0, 3] - (math.log(0.6) - math.log(0.75))) < 1e-12
+
+
+def test_nucleus_ties_at_the_cut_go_in_together():
+    # p = [0.4, 0.3, 0.3], top_p = 0.5: both tied tokens have 0.4 above them, so both are in
+    # the nucleus (a sorted prefix would keep only one, depending on the sort)
+    row = _logits_from_probs([0.4, 0.3, 0.3], 3)
+    res = _nucleus_single_row(row, [2, 1, 0], 0.5)
+    assert res["accepted"][0, 1:].tolist() == [True, True, True]
+    res = _nucleus_single_row(row, [2, 1, 0], 0.4)
+    assert res["accepted"][0, 1:].tolist() == [False, False, True]
+
+
+def test_nucleus_matches_a_sorted_prefix_without_ties():
+    # brute force: sort descending, keep the shortest prefix whose mass reaches top_p; on rows
+    # without ties a token is in it iff the mass strictly above it is below top_p
+    rng = rng_for(61, 0)
+    for trial in range(40):
+        V = int(rng.integers(2, 60))
+        row = rng.standard_normal(V) * 2.0
+        temp = float(rng.uniform(0.3, 2.0))
+        top_p = float(rng.uniform(0.05, 0.99))
+        z = row / temp
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        order = np.argsort(-p, kind="stable")
+        csum = np.cumsum(p[order])
+        j = int(np.searchsorted(csum, top_p)) + 1          # first prefix with mass >= top_p
+        inside = set(order[:j].tolist())
+        if any(abs(c - top_p) < 1e-9 for c in csum):
+            continue
+        kids = [int(x) for x in rng.choice(V, size=min(V, 6), replace=False)]
+        res = _nucleus_single_row(row, kids, top_p, temp)
+        assert res["accepted"][0, 1:].tolist() == [k in inside for k in kids], trial
+
+
+def test_nucleus_limits():
+    rng = rng_for(62, 0)
+    st = oracle.build_static(load_tree_choices("c1"), 10, 4)
+    V = 500
+    logits = rng.standard_normal((2, st["T"], V)).astype(np.float32) * 2
+    tokens = rng.integers(0, V, (2, st["T"])).tolist()
+    for b in range(2):
+        for c in range(1, st["T"]):             # some children are their parent row's argmax
+            if c % 3 == 0:
+                tokens[b][c] = int(np.argmax(logits[b, st["parent"][c]]))
+    greedy = oracle.typical_accept(logits, "f32", tokens, st, 0.0)
+    # a nucleus smaller than any probability holds only the maximum: greedy decisions
+    tiny = oracle.evaluate_posterior(logits, "f32", tokens, st, 0.7, top_p=1e-9,
+                                     sampling="nucleus")
+    assert np.array_equal(tiny["accepted"], greedy["accepted"])
+    assert tiny["accept_length"].tolist() == greedy["accept_length"].tolist()
+    # the whole distribution: every candidate with a finite logit is in it
+    full = oracle.evaluate_posterior(logits, "f32", tokens, st, 0.7, top_p=1.0,
+                                     sampling="nucleus")
+    assert full["accepted"].all()
+    assert full["accept_length"].tolist() == [max(st["path_len"])] * 2
+    # temperature 0 is greedy in nucleus mode too, and the fast flag changes nothing
+    g2 = oracle.evaluate_posterior(logits, "f32", tokens, st, 0.0, top_p=0.5, sampling="nucleus",
+                                   fast=True)
+    assert np.array_equal(g2["accepted"], greedy["accepted"])
+    typ = oracle.evaluate_posterior(logits, "f32", tokens, st, 0.7, sampling="typical", fast=True)
+    ref = oracle.typical_accept(logits, "f32", tokens, st, 0.7)
+    assert np.array_equal(typ["accepted"], ref["accepted"])
+
+
+def test_nucleus_widens_with_temperature():
+    # a hotter distribution is flatter, so the mass above a low-ranked token grows and fewer
+    # low-ranked candidates stay in a fixed-mass nucleus; at a very high temperature the mass
+    # above the rank-r token tends to r / V
+    row = np.linspace(3.0, -3.0, 50)
+    cold = _nucleus_single_row(row, list(range(50)), 0.9, temperature=0.5)
+    hot = _nucleus_single_row(row, list(range(50)), 0.9, temperature=5.0)
+    assert cold["accepted"][0, 1:].sum() < hot["accepted"][0, 1:].sum()
+    vhot = _nucleus_single_row(row, list(range(50)), 0.3, temperature=1e6)
+    assert vhot["accepted"][0, 1:].astype(int).tolist() == [1] * 15 + [0] * 35
