@@ -63,8 +63,9 @@ def kernel_bytes(cfg, T, n_int):
     return {
         "heads_w1": K * Hd * Hd * s + K * Hd * s + B * Hd * s + B * K * Hd * 4,
         "heads_w2": K * V * Hd * s + B * K * Hd * 4 + B * K * V * 4,
-        "topk": B * K * V * 4 + B * K * cfg.topk * 4,
-        "tree_gather": B * T * 8 + B * K * cfg.topk * 4,
+        # top-k (the logits re-read, the ids written) and, in the same launch, the tree gather
+        # (tokens and position ids written)
+        "topk": B * K * V * 4 + B * K * cfg.topk * 4 + B * T * 8,
         "attention": 2 * B * cfg.Hkv * (cfg.L + T) * cfg.D * s + 2 * B * cfg.Hq * T * cfg.D * s,
         "accept": B * n_int * V * s,
     }
@@ -298,9 +299,11 @@ class Workload:
         return events
 
     def kernel_names(self):
-        names = ["heads_w1", "heads_w2", "topk", "tree_gather", "attention", "accept"]
+        # the step's heads and tree run as one call, whose top-k merge also writes the tree
+        # tokens: "topk" times top-k and the gather together
+        names = ["heads_w1", "heads_w2", "topk", "attention", "accept"]
         if self.step.ws_attn.numel() > 256:
-            names.insert(5, "attn_combine")
+            names.insert(4, "attn_combine")
         return names
 
 

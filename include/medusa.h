@@ -249,6 +249,24 @@ int build_tree(const int32_t* choices, int n_choices, int max_depth, int K, int 
                int B, int static_ready, const medusa_tree* tree, int32_t* tokens,
                int32_t* position_ids, void* stream);
 
+/*
+ * medusa_heads (packed = 0) or medusa_heads_packed (packed = 1, bf16) followed by build_tree's
+ * per-step gather, in the same launches: the merge that finishes head d - 1's top-k writes the
+ * tokens and position ids of the tree's depth-d nodes, and head 0's merge writes the root.  The
+ * step's chain heads -> build_tree with one launch fewer (Wiblog page, tree-attention section:
+ * head d fills depth d).  Outputs are bit-identical to medusa_heads[_packed] followed by
+ * build_tree(static_ready = 1).  The tree's static arrays must already be on the device (one
+ * build_tree call with static_ready = 0).  Arguments: as medusa_heads / medusa_heads_packed and
+ * build_tree; the workspace is medusa_heads_workspace's.  Errors: theirs, and MEDUSA_ERR_TREE
+ * when tree->dmax > K or tree->max_rank >= topk.
+ */
+int medusa_heads_build_tree(const void* h, const void* w1, const void* b1, const void* w2,
+                            int dtype, int packed, int B, int hidden, long vocab, int K, int topk,
+                            const medusa_tree* tree, const int32_t* root_tokens,
+                            const int32_t* prefix_len, float* logits, int32_t* topk_ids,
+                            float* topk_logits, int32_t* tokens, int32_t* position_ids,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------------------- *
  * 3. Tree attention
  * ---------------------------------------------------------------------------------------- */

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     evaluate_posterior_workspace,
     load,
     medusa_heads,
+    medusa_heads_build_tree,
     medusa_heads_ex,
     medusa_heads_ex_workspace,
     medusa_heads_packed,

@@ -43,7 +43,7 @@ EXPORTS = ["medusa_last_error", "medusa_heads_workspace", "medusa_heads", "medus
            "medusa_stream_read", "commit_accepted", "tree_attention_rope_workspace",
            "tree_attention_rope", "medusa_sparse_tree", "medusa_heads_ex_workspace",
            "medusa_heads_ex", "typical_accept_noalloc", "evaluate_posterior_workspace",
-           "evaluate_posterior"]
+           "evaluate_posterior", "medusa_heads_build_tree"]
 
 SAMPLING = {"typical": 0, "nucleus": 1}
 
@@ -82,6 +82,9 @@ def load():
     L.typical_accept_workspace.argtypes = [i, i, l, i]
     L.typical_accept.restype = i
     L.typical_accept.argtypes = [vp, i, i, i, l, vp, tp, f, f, f, vp, vp, vp, vp, sz, vp]
+    L.medusa_heads_build_tree.restype = i
+    L.medusa_heads_build_tree.argtypes = [vp, vp, vp, vp, i, i, i, i, l, i, i, tp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, sz, vp]
     L.evaluate_posterior_workspace.restype = sz
     L.evaluate_posterior_workspace.argtypes = [i, l, tp, i]
     L.evaluate_posterior.restype = i
@@ -248,6 +251,23 @@ class Tree:
         c = self.c
         return dict(T=c.T, W=c.W, n_paths=c.n_paths, dmax=c.dmax, n_internal=c.n_internal,
                     max_rank=c.max_rank)
+
+
+def medusa_heads_build_tree(h, w1, b1, w2, vocab, K, topk, tree, root_tokens, prefix_len,
+                            topk_ids, tokens, position_ids, ws, logits=None, topk_logits=None,
+                            stream=None):
+    """medusa_heads (w1/w2 [K, out, in]) or medusa_heads_packed (flat packed w1/w2) and the
+    tree gather of build_tree in the same launches; the tree must already be uploaded."""
+    if not tree.static_ready:
+        raise ValueError("upload the tree first (one build_tree call)")
+    B, hd = h.shape
+    packed = 1 if w1.dim() == 1 else 0
+    _check(load().medusa_heads_build_tree(_ptr(h), _ptr(w1), _ptr(b1), _ptr(w2), dtype_code(h),
+                                          packed, B, hd, vocab, K, topk, ctypes.byref(tree.c),
+                                          _ptr(root_tokens), _ptr(prefix_len), _ptr(logits),
+                                          _ptr(topk_ids), _ptr(topk_logits), _ptr(tokens),
+                                          _ptr(position_ids), _ptr(ws), ws.numel(),
+                                          _stream(stream)))
 
 
 def build_tree(tree, topk_ids, root_tokens, prefix_len, tokens, position_ids, stream=None):

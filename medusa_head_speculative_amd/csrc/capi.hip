@@ -249,6 +249,45 @@ int medusa_heads_packed(const void* h, const void* w1_packed, const void* b1,
                   "medusa_heads_packed");
 }
 
+int medusa_heads_build_tree(const void* h, const void* w1, const void* b1, const void* w2,
+                            int dtype, int packed, int B, int hidden, long vocab, int K, int topk,
+                            const medusa_tree* tree, const int32_t* root_tokens,
+                            const int32_t* prefix_len, float* logits, int32_t* topk_ids,
+                            float* topk_logits, int32_t* tokens, int32_t* position_ids,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return fail(MEDUSA_ERR_DTYPE, "dtype = %d", dtype);
+  if (packed != 0 && packed != 1) return fail(MEDUSA_ERR_ARG, "packed must be 0 or 1");
+  if (packed && dtype != MEDUSA_BF16) return fail(MEDUSA_ERR_DTYPE, "packed weights are bf16");
+  if (!h || !w1 || !b1 || !w2 || !topk_ids || !tree || !root_tokens || !prefix_len || !tokens ||
+      !position_ids)
+    return fail(MEDUSA_ERR_ARG, "a required pointer is NULL");
+  if (!tree->depth || !tree->rank) return fail(MEDUSA_ERR_ARG, "tree->depth / tree->rank is NULL");
+  int rc = heads_shape(B, hidden, vocab, K, topk, packed != 0);
+  if (rc) return rc;
+  if (tree->T < 2 || tree->T > 4096) return fail(MEDUSA_ERR_TREE, "tree->T = %d", tree->T);
+  // the merge of head d - 1 writes the nodes of depth d from its candidates of rank < topk
+  if (tree->dmax < 1 || tree->dmax > K)
+    return fail(MEDUSA_ERR_TREE, "tree->dmax = %d does not fit K = %d", tree->dmax, K);
+  if (tree->max_rank < 0 || tree->max_rank >= topk)
+    return fail(MEDUSA_ERR_TREE, "tree->max_rank = %d does not fit topk = %d", tree->max_rank, topk);
+  const size_t need = medusa::heads_ws_layout(B, hidden, vocab, K, topk).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MEDUSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if ((rc = check_pending())) return rc;
+  medusa::TreeGather g;
+  g.depth = tree->depth;
+  g.rank = tree->rank;
+  g.root = root_tokens;
+  g.prefix_len = prefix_len;
+  g.tokens = tokens;
+  g.pos = position_ids;
+  g.T = tree->T;
+  return launched(medusa::launch_heads(h, w1, b1, w2, dtype, packed, B, hidden, vocab, K, topk,
+                                       logits, topk_ids, topk_logits, static_cast<char*>(workspace),
+                                       static_cast<hipStream_t>(stream), &g),
+                  "medusa_heads_build_tree");
+}
+
 // ---- tree -----------------------------------------------------------------------------------
 int medusa_tree_dims(const int32_t* choices, int n_choices, int max_depth, int K, int topk,
                      medusa_tree* tree) {

@@ -523,8 +523,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_chunks(const float* __restr
   if (lane < k) part[(static_cast<long>(row) * C + c) * k + lane] = mine;
 }
 
+// With g.tokens set, the merge wave of (sequence b, head kh) also writes the tree tokens and
+// position ids of depth kh + 1, which head kh fills (Wiblog, tree-attention section): node i of
+// that depth takes the candidate of rank rank[i], which lane rank[i] holds; the (b, 0) wave also
+// writes the root.  The same values as build_tree's gather, without its launch.
 __global__ __launch_bounds__(64) void topk_merge(const uint64_t* __restrict__ part, int k, int C,
-                                                 int32_t* __restrict__ ids, float* __restrict__ vals) {
+                                                 int32_t* __restrict__ ids, float* __restrict__ vals,
+                                                 int K, TreeGather g) {
   const int row = blockIdx.x, lane = threadIdx.x;
   const uint64_t* pr = part + static_cast<long>(row) * C * k;
   const long n = static_cast<long>(C) * k;
@@ -538,9 +543,30 @@ __global__ __launch_bounds__(64) void topk_merge(const uint64_t* __restrict__ pa
     }
     running = wave_select(keys, running, k);
   }
+  const int32_t id = static_cast<int32_t>(sel_key_index(running));
   if (lane < k) {
-    ids[static_cast<long>(row) * k + lane] = static_cast<int32_t>(sel_key_index(running));
+    ids[static_cast<long>(row) * k + lane] = id;
     if (vals) vals[static_cast<long>(row) * k + lane] = sel_key_value(running);
+  }
+  if (g.tokens) {
+    const int b = row / K, kh = row - b * K;
+    const int pl = g.prefix_len[b];
+    const int rt = g.root[b];
+    int32_t* tk = g.tokens + static_cast<long>(b) * g.T;
+    int32_t* ps = g.pos + static_cast<long>(b) * g.T;
+    for (int i0 = 0; i0 < g.T; i0 += 64) {
+      const int i = i0 + lane;
+      const int d = i < g.T ? g.depth[i] : -1;
+      const int r = i < g.T ? g.rank[i] : 0;
+      const int32_t cand = __shfl(id, r > 0 ? r : 0);      // every lane takes part in the shuffle
+      if (d == kh + 1) {
+        tk[i] = cand;
+        ps[i] = pl + d;
+      } else if (d == 0 && kh == 0) {
+        tk[i] = rt;
+        ps[i] = pl;
+      }
+    }
   }
 }
 
@@ -746,7 +772,7 @@ static void launch_packed(int variant, const uint16_t* Wp, const uint16_t* x, in
 hipError_t launch_heads_ex(const void* h, const void* w1, const void* b1, const void* gamma,
                            const void* beta, float eps, const void* w2, int dtype, int packed, int nb,
                            int B, int hd, long V, int K, int topk, float* logits, int32_t* topk_ids,
-                           float* topk_logits, char* ws, hipStream_t s) {
+                           float* topk_logits, char* ws, hipStream_t s, const TreeGather* gather) {
   const bool ln = gamma != nullptr;
   const HeadsWs L = heads_ws_layout(B, hd, V, K, topk, nb, ln);
   float* rb[2] = {reinterpret_cast<float*>(ws + L.r), reinterpret_cast<float*>(ws + L.r2)};
@@ -822,16 +848,18 @@ hipError_t launch_heads_ex(const void* h, const void* w1, const void* b1, const 
   hook_after(K_HEADS_W2, s);
   hook_before(K_TOPK, s);
   topk_chunks<<<dim3(L.chunks, B * K), kTopkThreads, 0, s>>>(lg, V, topk, L.chunks, part);
-  topk_merge<<<B * K, 64, 0, s>>>(part, topk, L.chunks, topk_ids, topk_logits);
+  topk_merge<<<B * K, 64, 0, s>>>(part, topk, L.chunks, topk_ids, topk_logits, K,
+                                  gather ? *gather : TreeGather{});
   hook_after(K_TOPK, s);
   return hipGetLastError();
 }
 
 hipError_t launch_heads(const void* h, const void* w1, const void* b1, const void* w2, int dtype,
                         int packed, int B, int hd, long V, int K, int topk, float* logits,
-                        int32_t* topk_ids, float* topk_logits, char* ws, hipStream_t s) {
+                        int32_t* topk_ids, float* topk_logits, char* ws, hipStream_t s,
+                        const TreeGather* gather) {
   return launch_heads_ex(h, w1, b1, nullptr, nullptr, 0.f, w2, dtype, packed, 1, B, hd, V, K, topk,
-                         logits, topk_ids, topk_logits, ws, s);
+                         logits, topk_ids, topk_logits, ws, s, gather);
 }
 
 }  // namespace medusa

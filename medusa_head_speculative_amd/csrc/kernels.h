@@ -28,13 +28,26 @@ struct HeadsWs {
   int chunks;
 };
 HeadsWs heads_ws_layout(int B, int hd, long V, int K, int topk, int nb = 1, int ln = 0);
+// The tree gather done by the top-k merge (tokens == nullptr: none): tokens and position ids of
+// every node from the merged candidates, as build_tree's gather computes them.
+struct TreeGather {
+  const int32_t* depth = nullptr;     // [T]
+  const int32_t* rank = nullptr;      // [T]
+  const int32_t* root = nullptr;      // [B]
+  const int32_t* prefix_len = nullptr;  // [B]
+  int32_t* tokens = nullptr;          // [B][T]
+  int32_t* pos = nullptr;             // [B][T]
+  int T = 0;
+};
 hipError_t launch_heads_ex(const void* h, const void* w1, const void* b1, const void* gamma,
                            const void* beta, float eps, const void* w2, int dtype, int packed, int nb,
                            int B, int hd, long V, int K, int topk, float* logits, int32_t* topk_ids,
-                           float* topk_logits, char* ws, hipStream_t s);
+                           float* topk_logits, char* ws, hipStream_t s,
+                           const TreeGather* gather = nullptr);
 hipError_t launch_heads(const void* h, const void* w1, const void* b1, const void* w2, int dtype,
                         int packed, int B, int hd, long V, int K, int topk, float* logits,
-                        int32_t* topk_ids, float* topk_logits, char* ws, hipStream_t s);
+                        int32_t* topk_ids, float* topk_logits, char* ws, hipStream_t s,
+                        const TreeGather* gather = nullptr);
 size_t packed_weight_bytes(int K, long rows, int hd);
 hipError_t launch_pack_weights(const void* w, int K, long rows, int hd, void* packed, hipStream_t s);
 

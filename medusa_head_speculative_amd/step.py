@@ -59,10 +59,21 @@ class VerifyStep:
                             self.accept_length, self.ws_acc,
                             next_token=self.next_token if next_token else None, stream=stream)
 
+    def heads_and_tree(self, h, w1, b1, w2, root_tokens, prefix_len, stream=None):
+        """heads then the tree tokens and position ids; once the tree is on the device, in the
+        same launches (medusa_heads_build_tree)."""
+        if not self.tree.static_ready:
+            self.heads(h, w1, b1, w2, stream)
+            self.build(root_tokens, prefix_len, stream)
+            return
+        _lib.medusa_heads_build_tree(h, w1, b1, w2, self.vocab, self.K, self.topk, self.tree,
+                                     root_tokens, prefix_len, self.topk_ids, self.tokens,
+                                     self.position_ids, self.ws_heads, logits=self.logits,
+                                     topk_logits=self.topk_logits, stream=stream)
+
     def run(self, *, h, w1, b1, w2, root_tokens, prefix_len, q, k_cache, v_cache, attn_out,
             verif_logits, temperature, eps=0.09, delta=0.3, stream=None):
-        self.heads(h, w1, b1, w2, stream)
-        self.build(root_tokens, prefix_len, stream)
+        self.heads_and_tree(h, w1, b1, w2, root_tokens, prefix_len, stream)
         self.attention(q, k_cache, v_cache, prefix_len, attn_out, stream)
         self.accept(verif_logits, temperature, eps, delta, stream=stream)
 
