@@ -61,6 +61,7 @@ hipError_t launch_tree_gather(const int32_t* topk_ids, int K, int topk, const in
 struct AttnPlan {
   int G;          // q heads per kv head
   int M;          // query rows per (b, kv head) = G * T
+  int rows;       // query rows per work-group (128, or 144 with nine one-block waves)
   int qtiles;     // work-group query tiles per (b, kv head)
   int splits;     // KV splits per (b, kv head, q tile)
   int nmb;        // 16-row blocks per wave of the bf16 kernel (1: 8 waves, 2: 4 waves)

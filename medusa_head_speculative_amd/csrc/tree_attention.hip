@@ -26,7 +26,8 @@
 
 namespace medusa {
 
-constexpr int kAttnRows = 128;   // query rows per work-group (4 waves x 32, or 8 x 16)
+constexpr int kAttnRows = 128;   // query rows per work-group (4 waves x 32, or 8 x 16) ...
+constexpr int kAttnRowsWide = 144;   // ... or 9 waves x 16 when that takes fewer query tiles
 constexpr int kKvTile = 64;
 constexpr int kMaxSplits = 16;
 // Work-groups at or above which the bf16 kernel keeps two row blocks per wave (4 waves of 32
@@ -125,7 +126,9 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kc,
                                            int lane) {
   constexpr int SLOTS = D / 8;                 // 16-byte chunks per row
   constexpr int RPI = 64 / SLOTS;              // rows per wave instruction
-  constexpr int INST = kKvTile / RPI / NW;     // instructions per wave per matrix
+  constexpr int NWL = NW < 8 ? NW : 8;         // loading waves (a ninth wave loads nothing)
+  constexpr int INST = kKvTile / RPI / NWL;    // instructions per wave per matrix
+  if (NW > NWL && wave >= NWL) return;
 #pragma unroll
   for (int u = 0; u < INST; ++u) {
     const int rbase = (wave * INST + u) * RPI;
@@ -149,15 +152,17 @@ __device__ __forceinline__ void issue_mask(const uint64_t* __restrict__ mask, in
   }
 }
 
-// NMB 16-row blocks per wave and NW = 8 / NMB waves, so a work-group always owns kAttnRows = 128
-// query rows: NMB = 2 keeps more rows per wave, NMB = 1 twice the waves (half the registers each,
-// so four waves share a SIMD).
-template <int D, bool ROPE, int NMB>
-__global__ __launch_bounds__(512 / NMB, 2) void tree_attn_bf16(AttnArgs a) {
-  constexpr int NW = 8 / NMB;            // waves per work-group
+// NMB 16-row blocks per wave and NW waves, so a work-group owns ROWS = NW * 16 * NMB query rows:
+// 128 with NW = 8 / NMB (NMB = 2 keeps more rows per wave, NMB = 1 twice the waves with half the
+// registers each, so four waves share a SIMD), or 144 with nine waves of one block, when a
+// (sequence, kv head) has a few rows past a multiple of 128 that would otherwise take a query
+// tile of their own and stream the whole K/V range once more.
+template <int D, bool ROPE, int NMB, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int RPW = NMB * 16;          // query rows per wave
-  static_assert(NW * RPW == kAttnRows, "a work-group owns kAttnRows rows");
+  constexpr int ROWS = NW * RPW;         // query rows per work-group
+  static_assert(ROWS == kAttnRows || ROWS == kAttnRowsWide, "a work-group owns 128 or 144 rows");
   constexpr int NKB = D / 32;            // 32-wide contraction blocks over the head dim
   constexpr int NDB = D / 16;            // 16-wide output blocks over the head dim
   constexpr int TILE = kKvTile * D;      // elements per K (or V) tile
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(512 / NMB, 2) void tree_attn_bf16(AttnArgs a) {
   __shared__ __align__(16) uint16_t K1[TILE];
   __shared__ __align__(16) uint16_t V1[TILE];
   __shared__ int s_active[64];
-  __shared__ __align__(16) uint64_t s_mask[2][kAttnRows];   // mask words of the tree tile in flight
+  __shared__ __align__(16) uint64_t s_mask[2][ROWS];   // mask words of the tree tile in flight
 
   // ---- work item; consecutive logical items (query tiles of one K/V range) share an XCD ----
   const int per_xcd = gridDim.x >> 3;
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(512 / NMB, 2) void tree_attn_bf16(AttnArgs a) {
     __syncthreads();
     // four mask words per thread in flight at once (a slot past the rows reads word 0, always
     // valid, and is ignored)
-    for (int p0 = tid; p0 < kAttnRows * ntt; p0 += 4 * NT) {
+    for (int p0 = tid; p0 < ROWS * ntt; p0 += 4 * NT) {
       uint64_t w[4];
       int tt[4];
       bool ok[4];
@@ -209,8 +214,8 @@ __global__ __launch_bounds__(512 / NMB, 2) void tree_attn_bf16(AttnArgs a) {
         const int p = p0 + u * NT;
         const int r = p / ntt;
         tt[u] = p - r * ntt;
-        const int m = qt * kAttnRows + r;
-        ok[u] = p < kAttnRows * ntt && m < a.M;
+        const int m = qt * ROWS + r;
+        ok[u] = p < ROWS * ntt && m < a.M;
         w[u] = a.mask[ok[u] ? static_cast<long>(m / a.G) * a.W + tt[u] : 0];
       }
 #pragma unroll
@@ -234,9 +239,9 @@ __global__ __launch_bounds__(512 / NMB, 2) void tree_attn_bf16(AttnArgs a) {
   };
 
   // node whose mask word this lane stages: row wave*RPW + lane/2 of the work-group
-  const int mrow_m = qt * kAttnRows + wave * RPW + (lane >> 1);
+  const int mrow_m = qt * ROWS + wave * RPW + (lane >> 1);
   // a wave whose rows are all past M only helps stage tiles and meets the barriers
-  const bool wave_active = qt * kAttnRows + wave * RPW < a.M;
+  const bool wave_active = qt * ROWS + wave * RPW < a.M;
   const int mrow_node = mrow_m < a.M ? mrow_m / a.G : 0;
 
   int t = next_active(t_begin);
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(512 / NMB, 2) void tree_attn_bf16(AttnArgs a) {
   bf16x8_t qf[NMB][NKB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
-    const int m = qt * kAttnRows + wave * RPW + mb * 16 + mm;
+    const int m = qt * ROWS + wave * RPW + mb * 16 + mm;
     rvalid[mb] = m < a.M;
     node[mb] = rvalid[mb] ? m / a.G : 0;
     const int hq = kvh * a.G + (rvalid[mb] ? m % a.G : 0);
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(512 / NMB, 2) void tree_attn_bf16(AttnArgs a) {
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     const float l = lacc[mb][0];
-    const int m = qt * kAttnRows + wave * RPW + mb * 16 + mm;
+    const int m = qt * ROWS + wave * RPW + mb * 16 + mm;
     if (!rvalid[mb]) continue;
     if (a.splits == 1) {
       const float inv = 1.f / l;
@@ -672,15 +677,34 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
   AttnPlan p{};
   p.G = Hq / Hkv;
   p.M = p.G * T;
+  p.rows = kAttnRows;
   p.qtiles = (p.M + kAttnRows - 1) / kAttnRows;
   p.splits = 1;
   if (dtype == 1) {
+    // 144-row work-groups (nine waves of one row block) when they take fewer query tiles than
+    // 128-row ones, leave enough work-groups that the K/V range needs no split, and keep the grid
+    // in the one-block-per-wave range.  At 118 VGPRs only one nine-wave work-group fits on a CU;
+    // still, on the 33B shape (129 rows per kv head: a 128-row tile and a 1-row tile that streams
+    // the whole K/V range again) attention went from 157.5 to 137.8 us.  Forcing two per CU
+    // (96 VGPRs, a few spilled) took 146.7 us.  On the Llama-8B shape (260 rows, split grid) the
+    // attention kernel gained 1 us and the merge of 16 splits instead of 10 lost 2.  Setting
+    // MEDUSA_ATTN_ROWS to 128 or 144 forces the choice where it is possible.
+    static const int forced_rows = [] { const char* v = getenv("MEDUSA_ATTN_ROWS"); return v ? atoi(v) : 0; }();
+    static const long target = wg_target_from_env();
+    const int q144 = (p.M + kAttnRowsWide - 1) / kAttnRowsWide;
+    const bool small_grid = static_cast<long>(B) * Hkv * p.qtiles < kAttnTwoBlockUnits;
+    const bool unsplit = static_cast<long>(B) * Hkv * q144 >= target;
+    const bool wide = forced_rows == kAttnRowsWide ? small_grid
+                    : forced_rows == kAttnRows ? false : small_grid && unsplit && q144 < p.qtiles;
+    if (wide) {
+      p.rows = kAttnRowsWide;
+      p.qtiles = q144;
+    }
     const long units = static_cast<long>(B) * Hkv * p.qtiles;
     const int ntiles = (max_prefix_len + kKvTile - 1) / kKvTile + (T + kKvTile - 1) / kKvTile;
     // too few units to cover the CUs: split the K/V range until the grid reaches the target
     // (256 work-groups, one per CU, unless MEDUSA_ATTN_WG_TARGET says otherwise), keeping at
     // least two tiles per split
-    static const long target = wg_target_from_env();
     if (units < target) {
       long s = target / units;
       s = s < ntiles / 2 ? s : ntiles / 2;
@@ -688,10 +712,10 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
       p.splits = s < 1 ? 1 : static_cast<int>(s);
     }
   }
-  p.nmb = static_cast<long>(B) * Hkv * p.qtiles * p.splits >= kAttnTwoBlockUnits ? 2 : 1;
+  p.nmb = p.rows == kAttnRows && static_cast<long>(B) * Hkv * p.qtiles * p.splits >= kAttnTwoBlockUnits ? 2 : 1;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
-  const size_t rows = static_cast<size_t>(p.splits) * B * Hkv * p.qtiles * kAttnRows;
+  const size_t rows = static_cast<size_t>(p.splits) * B * Hkv * p.qtiles * p.rows;
   p.ws_o = take(p.splits > 1 ? rows * D * sizeof(float) : 0);
   p.ws_ml = take(p.splits > 1 ? rows * sizeof(float2) : 0);
   p.total = off;
@@ -737,7 +761,7 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
   a.W = W;
   a.G = P.G;
   a.M = P.M;
-  a.Mpad = P.qtiles * kAttnRows;
+  a.Mpad = P.qtiles * P.rows;
   a.qtiles = P.qtiles;
   a.splits = P.splits;
   a.nwork = B * Hkv * P.qtiles * P.splits;
@@ -746,23 +770,22 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
   a.rope_cs = rope_cs;
   const unsigned grid = static_cast<unsigned>(((a.nwork + 7) / 8) * 8);
   hook_before(K_ATTENTION, s);
-  if (P.nmb == 1) {
-    if (rope_cs) {
-      if (D == 128) tree_attn_bf16<128, true, 1><<<grid, 512, 0, s>>>(a);
-      else tree_attn_bf16<64, true, 1><<<grid, 512, 0, s>>>(a);
-    } else {
-      if (D == 128) tree_attn_bf16<128, false, 1><<<grid, 512, 0, s>>>(a);
-      else tree_attn_bf16<64, false, 1><<<grid, 512, 0, s>>>(a);
-    }
-  } else {
-    if (rope_cs) {
-      if (D == 128) tree_attn_bf16<128, true, 2><<<grid, 256, 0, s>>>(a);
-      else tree_attn_bf16<64, true, 2><<<grid, 256, 0, s>>>(a);
-    } else {
-      if (D == 128) tree_attn_bf16<128, false, 2><<<grid, 256, 0, s>>>(a);
-      else tree_attn_bf16<64, false, 2><<<grid, 256, 0, s>>>(a);
-    }
+#define MEDUSA_ATTN_LAUNCH(NMB_, NW_)                                                        \
+  if (rope_cs) {                                                                          \
+    if (D == 128) tree_attn_bf16<128, true, NMB_, NW_><<<grid, NW_ * 64, 0, s>>>(a);      \
+    else tree_attn_bf16<64, true, NMB_, NW_><<<grid, NW_ * 64, 0, s>>>(a);                \
+  } else {                                                                                \
+    if (D == 128) tree_attn_bf16<128, false, NMB_, NW_><<<grid, NW_ * 64, 0, s>>>(a);     \
+    else tree_attn_bf16<64, false, NMB_, NW_><<<grid, NW_ * 64, 0, s>>>(a);               \
   }
+  if (P.rows == kAttnRowsWide) {
+    MEDUSA_ATTN_LAUNCH(1, 9)
+  } else if (P.nmb == 1) {
+    MEDUSA_ATTN_LAUNCH(1, 8)
+  } else {
+    MEDUSA_ATTN_LAUNCH(2, 4)
+  }
+#undef MEDUSA_ATTN_LAUNCH
   hook_after(K_ATTENTION, s);
   if (P.splits > 1) {
     hook_before(K_ATTN_COMBINE, s);

@@ -68,6 +68,10 @@ CASES = [
     ("bf16", 3, 64, 8, 128, "c4", [3, 40, 64]),
     ("bf16", 3, 64, 8, 64, "c4", [0, 17, 65]),
     ("bf16", 2, 4, 4, 128, "one", [0, 3]),
+    # 129 and 130 query rows per kv head with 256 (sequence, kv head) pairs: one 144-row
+    # work-group of nine waves each, instead of a 128-row tile and a 1- or 2-row one
+    ("bf16", 2, 128, 128, 128, "c3", [64, 200]),
+    ("bf16", 4, 128, 64, 64, "c1", [0, 1, 100, 63]),
     ("f32", 2, 4, 2, 64, "c1", [0, 77]),
     ("f32", 1, 2, 2, 128, "c0", [1]),
     ("f32", 1, 8, 1, 64, "c3", [200]),
