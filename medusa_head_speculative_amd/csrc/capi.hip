@@ -1,6 +1,10 @@
 // C ABI of libmedusa_hip: argument validation, error reporting, workspace sizing, the host-side
 // static tree, and dispatch to the kernel launchers.  Every check runs before any launch, so a
-// rejected call writes nothing.
+// rejected call writes nothing.  A checked host build (-DMEDUSA_CHECKED) turns on the standard
+// library's bounds assertions on every container access of the host code (tree parsing).
+#ifdef MEDUSA_CHECKED
+#define _GLIBCXX_ASSERTIONS 1
+#endif
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

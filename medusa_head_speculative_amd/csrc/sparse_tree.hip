@@ -12,6 +12,11 @@
 // Best-first search: the heap holds the children of the nodes taken so far; the next node taken
 // is the heap's best, which is the next node in the global order, since every node ranks below
 // its parent.  Probabilities are products in depth order (fp64), so equal products tie exactly.
+// A checked host build (-DMEDUSA_CHECKED) turns on the standard library's bounds assertions on
+// every container access below.
+#ifdef MEDUSA_CHECKED
+#define _GLIBCXX_ASSERTIONS 1
+#endif
 #include <algorithm>
 #include <cstdint>
 #include <queue>

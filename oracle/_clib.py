@@ -8,7 +8,8 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "medusa_oracle.c")
-LIB = os.path.join(HERE, "liboracle.so")
+# MEDUSA_ORACLE_LIB names another build of the same source (the sanitizer test's), used as is
+LIB = os.environ.get("MEDUSA_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 DT = {"f32": 0, "bf16": 1}
 
@@ -27,6 +28,8 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB):
+            if os.environ.get("MEDUSA_ORACLE_LIB"):
+                raise FileNotFoundError(LIB)
             build()
         L = ctypes.CDLL(LIB)
         vp, dp, ip = ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p
