@@ -554,17 +554,32 @@ __global__ __launch_bounds__(64) void topk_merge(const uint64_t* __restrict__ pa
     const int rt = g.root[b];
     int32_t* tk = g.tokens + static_cast<long>(b) * g.T;
     int32_t* ps = g.pos + static_cast<long>(b) * g.T;
-    for (int i0 = 0; i0 < g.T; i0 += 64) {
-      const int i = i0 + lane;
-      const int d = i < g.T ? g.depth[i] : -1;
-      const int r = i < g.T ? g.rank[i] : 0;
-      const int32_t cand = __shfl(id, r > 0 ? r : 0);      // every lane takes part in the shuffle
-      if (d == kh + 1) {
-        tk[i] = cand;
-        ps[i] = pl + d;
-      } else if (d == 0 && kh == 0) {
-        tk[i] = rt;
-        ps[i] = pl;
+    // Eight 64-node slices per pass: all their depth / rank loads are issued before the first
+    // store (the stores could alias the static arrays as far as the compiler knows, so a
+    // one-slice loop would wait out a full load latency per slice).  Lanes past the end read the
+    // last node and are masked by depth -1.
+    constexpr int kSlices = 8;
+    for (int i0 = 0; i0 < g.T; i0 += 64 * kSlices) {
+      int d[kSlices], r[kSlices];
+#pragma unroll
+      for (int u = 0; u < kSlices; ++u) {
+        const int i = i0 + u * 64 + lane;
+        const int ic = i < g.T ? i : g.T - 1;
+        d[u] = g.depth[ic];
+        r[u] = g.rank[ic];
+        if (i >= g.T) d[u] = -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kSlices; ++u) {
+        const int i = i0 + u * 64 + lane;
+        const int32_t cand = __shfl(id, r[u] > 0 ? r[u] : 0);   // every lane takes part
+        if (d[u] == kh + 1) {
+          tk[i] = cand;
+          ps[i] = pl + d[u];
+        } else if (d[u] == 0 && kh == 0) {
+          tk[i] = rt;
+          ps[i] = pl;
+        }
       }
     }
   }
