@@ -66,6 +66,37 @@ def sample_units(B, Hq, T, n, seed):
     return np.array(sorted(set(sel)), np.int32)
 
 
+def attention_all_f32(q, kc, vc, prefix_len, mask_words, Hkv):
+    """Every output of tree attention from plain float32 PyTorch ops on the device: node n of
+    sequence b attends to the b's prefix rows and the tree rows its mask word selects, with
+    softmax(q k^T / sqrt(D)) v (Wiblog, tree-attention section).  A test reference for checking
+    all outputs at sizes the fp64 oracle can only sample; tests pin it to the oracle on the
+    sampled units first.  Returns float64 [B, Hq, T, D]."""
+    import torch
+    torch.backends.cuda.matmul.allow_tf32 = False
+    B, Hq, T, D = q.shape
+    G = Hq // Hkv
+    words = np.ascontiguousarray(np.asarray(mask_words, np.uint64).reshape(T, -1))
+    bits = np.unpackbits(words.view(np.uint8), axis=1, bitorder="little")[:, :T].astype(bool)
+    vis_tree = torch.from_numpy(bits).cuda()
+    qd, kd, vd = dev(q).float(), dev(kc).float(), dev(vc).float()
+    out = torch.empty((B, Hq, T, D), dtype=torch.float32, device="cuda")
+    scale = 1.0 / np.sqrt(D)
+    for b in range(B):
+        L = int(prefix_len[b])
+        vis = torch.cat([torch.ones((T, L), dtype=torch.bool, device="cuda"), vis_tree], 1)
+        for g in range(Hkv):
+            k = kd[b, g, :L + T].contiguous()
+            v = vd[b, g, :L + T].contiguous()
+            qq = qd[b, g * G:(g + 1) * G].reshape(G * T, D).contiguous()
+            s = (qq @ k.t().contiguous()) * scale
+            s = s.view(G, T, L + T).masked_fill(~vis.unsqueeze(0), float("-inf"))
+            p = torch.softmax(s, dim=-1).reshape(G * T, L + T)
+            out[b, g * G:(g + 1) * G] = (p @ v).view(G, T, D)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
 def mask_array(static):
     return np.array(static["mask"], dtype=np.uint64)
 

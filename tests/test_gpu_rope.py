@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import as_f64, dev, host, lib, mask_array, say, tol
+from gpu_util import as_f64, attention_all_f32, dev, host, lib, mask_array, say, tol
 from synth import get_config
 from synth.configs import custom
 from synth.gen import gen_attention_inputs
@@ -70,8 +70,18 @@ def test_rope_attention_full_size(ci, base):
     ref = oracle.tree_attention(qr, kr, a["v_cache"], cfg.dtype, a["prefix_len"], st["mask"],
                                 cfg.Hkv, sel=sel)
     got = as_f64(out, cfg.dtype)
+    assert not np.isnan(got).any()
     if sel is not None:
-        got, ref = got[sel[:, 0], sel[:, 1], sel[:, 2]], ref[sel[:, 0], sel[:, 1], sel[:, 2]]
+        ref = ref[sel[:, 0], sel[:, 1], sel[:, 2]]
+        # every output against a float32 device reference over the oracle's rotated q and keys,
+        # pinned to the oracle on the sampled units
+        every = attention_all_f32(qr, kr, a["v_cache"], a["prefix_len"], mask_array(st), cfg.Hkv)
+        pin = float(np.abs(every[sel[:, 0], sel[:, 1], sel[:, 2]] - ref).max())
+        assert pin <= 1e-4, pin
+        err_all = float(np.abs(got - every).max())
+        print(f"{cfg.name}: max |out - f32 reference| = {err_all:.3e} over {got.size} values")
+        assert err_all <= tol(cfg.dtype)
+        got = got[sel[:, 0], sel[:, 1], sel[:, 2]]
     err = float(np.abs(got - ref).max())
     print(f"{cfg.name}: max |out - oracle| = {err:.3e}")
     assert err <= tol(cfg.dtype)
