@@ -437,11 +437,27 @@ def main():
     m.set_kernel_events("rope", None, None)
     m.set_kernel_events("attention", None, None)
     del kc_rope, out_rope, ws_rope
+    # the nucleus mode of evaluate_posterior (top_p 0.9) on the step's logits and tree tokens,
+    # its three acceptance launches together ("accept_nucleus"; at temperature 0 both modes are
+    # the greedy one, so it runs at 0.7 there)
+    ws_nuc = m.workspace(m.evaluate_posterior_workspace(cfg.B, cfg.V, step.tree, "nucleus"))
+    nuc_out = [torch.empty((cfg.B,), dtype=torch.int32, device="cuda") for _ in range(3)]
+    nuc_temp = temperature if temperature > 0 else 0.7
+    events["accept_nucleus"] = w.make_events(nb)
+    for i in range(nb):
+        m.set_kernel_events("accept", *events["accept_nucleus"][i])
+        m.evaluate_posterior(w.logits, step.tokens, step.tree, nuc_temp, cfg.eps, cfg.delta,
+                             nuc_out[0], nuc_out[1], ws_nuc, top_p=0.9, sampling="nucleus",
+                             next_token=nuc_out[2])
+    torch.cuda.synchronize()
+    m.set_kernel_events("accept", None, None)
+    del ws_nuc, nuc_out
     kb = kernel_bytes(cfg, T, n_int)
     # rope: every tree key row read and written once, and each node's cos/sin written (fp32);
     # attention_rope: the attention's bytes plus that table, read once
     kb["rope"] = 2 * cfg.B * cfg.Hkv * T * cfg.D * cfg.esize + cfg.B * T * cfg.D * 4
     kb["attention_rope"] = kb["attention"] + cfg.B * T * cfg.D * 4
+    kb["accept_nucleus"] = kb["accept"]
     # commit: each accepted node's K and V rows read and written once, plus the emitted tokens
     moved = int(step.accept_length.cpu().numpy().sum())
     kb["commit"] = 4 * moved * cfg.Hkv * cfg.D * cfg.esize + cfg.B * (step.tree.dims["dmax"] + 1) * 4
