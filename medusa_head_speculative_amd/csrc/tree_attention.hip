@@ -117,26 +117,45 @@ __device__ __forceinline__ int v_frag_base(int lg, int mm) {
   return r * D + ((((mm & 3) >> 1) ^ key) & 1) * 8 + (mm & 1) * 4 + ((key >> 1) << 4);
 }
 
-// Async loads of one 64-row K/V tile straight into LDS (no registers).  Rows past nvalid repeat
-// the last valid row: finite data whose scores the mask removes.
+// Async loads of one 64-row K/V tile straight into LDS (no registers), as buffer loads: the
+// buffer descriptors (scalar) start at the tile's first row and cover its nvalid valid rows, so
+// rows past them read as zeros (finite data whose scores the mask removes; no clamp), and each
+// lane's byte offset inside the tile is the same for every tile (tile_voffsets, computed once).
+// No vector instruction per tile besides the loads.
+template <int D, int NW>
+struct TileLoad {
+  static constexpr int SLOTS = D / 8;                 // 16-byte chunks per row
+  static constexpr int RPI = 64 / SLOTS;              // rows per wave instruction
+  static constexpr int NWL = NW < 8 ? NW : 8;         // loading waves (a ninth wave loads nothing)
+  static constexpr int INST = kKvTile / RPI / NWL;    // instructions per wave per matrix
+};
+
+template <int D, int NW>
+__device__ __forceinline__ void tile_voffsets(int wave, int lane, int (&voff)[TileLoad<D, NW>::INST]) {
+  using TL = TileLoad<D, NW>;
+#pragma unroll
+  for (int u = 0; u < TL::INST; ++u) {
+    const int r = (wave * TL::INST + u) * TL::RPI + lane / TL::SLOTS;
+    const int c = (lane % TL::SLOTS) ^ slot_key<D>(r);
+    voff[u] = (r * D + c * 8) * 2;
+  }
+}
+
 template <int D, int NW>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kc,
                                            const uint16_t* __restrict__ vc, long rowbase,
                                            int nvalid, uint16_t* Kd, uint16_t* Vd, int wave,
-                                           int lane) {
-  constexpr int SLOTS = D / 8;                 // 16-byte chunks per row
-  constexpr int RPI = 64 / SLOTS;              // rows per wave instruction
-  constexpr int NWL = NW < 8 ? NW : 8;         // loading waves (a ninth wave loads nothing)
-  constexpr int INST = kKvTile / RPI / NWL;    // instructions per wave per matrix
-  if (NW > NWL && wave >= NWL) return;
+                                           const int* voff) {
+  using TL = TileLoad<D, NW>;
+  if (NW > TL::NWL && wave >= TL::NWL) return;
+  const int bytes = nvalid * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + rowbase * D), 0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + rowbase * D), 0, bytes, 0x00020000);
 #pragma unroll
-  for (int u = 0; u < INST; ++u) {
-    const int rbase = (wave * INST + u) * RPI;
-    const int r = rbase + lane / SLOTS;
-    const int c = (lane % SLOTS) ^ slot_key<D>(r);
-    const long goff = (rowbase + min(r, nvalid - 1)) * D + c * 8;
-    __builtin_amdgcn_global_load_lds(kc + goff, (__attribute__((address_space(3))) void*)(Kd + rbase * D), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vc + goff, (__attribute__((address_space(3))) void*)(Vd + rbase * D), 16, 0, 0);
+  for (int u = 0; u < TL::INST; ++u) {
+    const int rbase = (wave * TL::INST + u) * TL::RPI;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Kd + rbase * D), 16, voff[u], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vd + rbase * D), 16, voff[u], 0, 0, 0);
   }
 }
 
@@ -184,7 +203,8 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
   const int kvh = rest % a.Hkv;
   const int b = rest / a.Hkv;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
   const int lg = lane >> 4, mm = lane & 15;
   const int L = min(max(a.prefix_len[b], 0), a.Lmax);   // callers promise prefix_len <= Lmax
   const int np = (L + kKvTile - 1) / kKvTile;
@@ -224,9 +244,9 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
     }
     __syncthreads();
   }
-  auto next_active = [&](int t) {
+  auto next_active = [&](int t) {   // (uniform: every thread reads the same flags)
     while (t < t_end && t >= np && !s_active[t - np]) ++t;
-    return t;
+    return __builtin_amdgcn_readfirstlane(t);
   };
   auto tile_rows = [&](int t, long& row0, int& nvalid) {   // first cache row, valid rows
     if (t < np) {
@@ -244,13 +264,15 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
   const bool wave_active = qt * ROWS + wave * RPW < a.M;
   const int mrow_node = mrow_m < a.M ? mrow_m / a.G : 0;
 
+  int voff[TileLoad<D, NW>::INST];   // this lane's byte offsets inside a tile
+  tile_voffsets<D, NW>(wave, lane, voff);
   int t = next_active(t_begin);
   int buf = 0;
   if (t < t_end) {
     long row0;
     int nvalid;
     tile_rows(t, row0, nvalid);
-    issue_tile<D, NW>(a.kc, a.vc, kvbase + row0, nvalid, K0, V0, wave, lane);
+    issue_tile<D, NW>(a.kc, a.vc, kvbase + row0, nvalid, K0, V0, wave, voff);
     if (t >= np) issue_mask<RPW>(a.mask, a.W, t - np, mrow_node, s_mask[0], wave, lane);
   }
 
@@ -343,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
       long nrow0;
       int nnvalid;
       tile_rows(tn, nrow0, nnvalid);
-      issue_tile<D, NW>(a.kc, a.vc, kvbase + nrow0, nnvalid, Kn, Vn, wave, lane);
+      issue_tile<D, NW>(a.kc, a.vc, kvbase + nrow0, nnvalid, Kn, Vn, wave, voff);
       if (tn >= np) issue_mask<RPW>(a.mask, a.W, tn - np, mrow_node, s_mask[buf ^ 1], wave, lane);
     }
     if (!wave_active) {
