@@ -708,7 +708,8 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
     // in the one-block-per-wave range.  At 118 VGPRs only one nine-wave work-group fits on a CU;
     // still, on the 33B shape (129 rows per kv head: a 128-row tile and a 1-row tile that streams
     // the whole K/V range again) attention went from 157.5 to 137.8 us.  Forcing two per CU
-    // (96 VGPRs, a few spilled) took 146.7 us.  On the Llama-8B shape (260 rows, split grid) the
+    // (five waves per SIMD: 96 VGPRs, 3 spilled, with the buffer-load tiles) took 138-140 us
+    // against 135.5-136.2 on the same GPU.  On the Llama-8B shape (260 rows, split grid) the
     // attention kernel gained 1 us and the merge of 16 splits instead of 10 lost 2.  Setting
     // MEDUSA_ATTN_ROWS to 128 or 144 forces the choice where it is possible.
     static const int forced_rows = [] { const char* v = getenv("MEDUSA_ATTN_ROWS"); return v ? atoi(v) : 0; }();
