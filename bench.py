@@ -249,12 +249,34 @@ class Workload:
         t = t.cuda()
         return t.view(self.torch.bfloat16) if a.dtype == np.uint16 else t
 
-    def run(self, temp):
+    def run_kwargs(self, temp):
         cfg = self.cfg
-        self.step.run(h=self.h, w1=self.w1, b1=self.b1, w2=self.w2, root_tokens=self.root,
-                      prefix_len=self.pl, q=self.q, k_cache=self.kc, v_cache=self.vc,
-                      attn_out=self.out, verif_logits=self.logits, temperature=temp,
-                      eps=cfg.eps, delta=cfg.delta)
+        return dict(h=self.h, w1=self.w1, b1=self.b1, w2=self.w2, root_tokens=self.root,
+                    prefix_len=self.pl, q=self.q, k_cache=self.kc, v_cache=self.vc,
+                    attn_out=self.out, verif_logits=self.logits, temperature=temp,
+                    eps=cfg.eps, delta=cfg.delta)
+
+    def run(self, temp):
+        self.step.run(**self.run_kwargs(temp))
+
+    def timed_graph(self, temp, steps, warmup):
+        """The same steps replayed from a HIP graph of one step (VerifyStep.capture): one host
+        call per step.  Returns {steps_per_s, ms_per_step}, or the error if capture failed."""
+        torch = self.torch
+        try:
+            graph = self.step.capture(**self.run_kwargs(temp))
+        except Exception as e:          # reported, not fatal: the eager figures stand alone
+            return {"error": f"{type(e).__name__}: {e}"}
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        del graph
+        return {"steps_per_s": round(steps / dt, 2), "ms_per_step": round(dt / steps * 1e3, 5)}
 
     def make_events(self, n):
         torch = self.torch
@@ -350,7 +372,7 @@ def measure_light(m, torch, ci, oracle_on, cpu_threads):
            "w2": {"avg_launch_ms": round(w2_ms, 5),
                   "GB/s": round(kb["heads_w2"] / (w2_ms * 1e-3) / 1e9, 1),
                   "hbm_frac": round(kb["heads_w2"] / (w2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-           "kernels": kernels}
+           "kernels": kernels, "graph": w.timed_graph(temperature, steps, 5)}
     if cfg.temps[0] == 0.0 and temperature != 0.0:
         dt0, _ = w.timed(0.0, max(5, steps // 2), warmup=2)
         a0 = w.step.accept_length.cpu().numpy()
@@ -481,6 +503,7 @@ def main():
 
     nd = max(10, min(args.steps, 100))
     warm = per_step(nd)
+    graph_rate = w.timed_graph(temperature, args.steps, 5)
     flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     cold = per_step(nd, flush)
     del flush
@@ -595,7 +618,7 @@ def main():
         "accepted_tokens_per_s": round(steps_per_s * emitted, 1),
         "w2": {"avg_launch_ms": round(w2_ms, 5), "GB/s": roofline["achieved"],
                "hbm_frac": roofline["frac"]},
-        "kernels": {k: kernels[k] for k in w.kernel_names()}, "greedy": t0g}
+        "kernels": {k: kernels[k] for k in w.kernel_names()}, "graph": graph_rate, "greedy": t0g}
 
     # ---- the oracle on the host's cores: whole steps at the OpenMP thread count in force (the
     #      headline baseline), then at one thread ----
@@ -668,6 +691,7 @@ def main():
         "kernels": kernels,
         "heads_variant": head_variant,
         "step_time_warm": warm,
+        "graph_replay": graph_rate,
         "step_time_mall_flushed": cold,
         "tree": {"ancestors_or_self": anc, "internal_rows": n_int,
                  "sparse_tree_host_us": round(sparse_us, 1),

@@ -77,6 +77,24 @@ class VerifyStep:
         self.attention(q, k_cache, v_cache, prefix_len, attn_out, stream)
         self.accept(verif_logits, temperature, eps, delta, stream=stream)
 
+    def capture(self, **run_kwargs):
+        """run(**run_kwargs) recorded into a HIP graph (a torch.cuda.CUDAGraph), to be replayed
+        with the same buffers: one host call per step instead of one per launch, for steps small
+        enough that issuing the launches costs more than running them.  The step allocates,
+        copies and clears nothing once the tree is on the device (an eager run first puts it
+        there), so the graph holds kernel nodes only.  Replays read whatever the input buffers
+        hold at replay time."""
+        if not self.tree.static_ready:
+            self.run(**run_kwargs)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=side):
+            self.run(**run_kwargs)
+        torch.cuda.current_stream().wait_stream(side)
+        return graph
+
     def commit(self, k_cache, v_cache, prefix_len, hidden=None, next_hidden=None, stream=None):
         """After accept: emit the accepted tokens (out_tokens, out_count), move their K/V rows
         into place, and set new_prefix_len / new_root (and next_hidden from hidden)."""
