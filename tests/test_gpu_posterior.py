@@ -133,3 +133,27 @@ def test_nucleus_limits_and_typical_mode():
     assert all(np.array_equal(x, host(y)) for x, y in zip(typ, ref))
     print(f"top_p=1 accept_length {full[1].tolist()}, tiny top_p {tiny[1].tolist()}, "
           f"greedy {greedy['accept_length'].tolist()}")
+
+
+@pytest.mark.parametrize("ci,nseeds", [(0, 16), (1, 16), (2, 8)])
+def test_nucleus_seed_sweep(ci, nseeds):
+    """The nucleus mode over fresh tree tokens and verification logits per seed, top_p cycling
+    through 0.5, 0.8, 0.9 and 0.95, temperature 0.7: every result equals the oracle's up to the
+    decisions inside the 1e-4 band, whose number is bounded (at most 1 in 500, and at least 2)."""
+    cfg = get_config(ci)
+    m = lib()
+    choices = load_tree_choices(f"c{ci}")
+    banded = decisions = 0
+    for j in range(nseeds):
+        seed = 300 + j
+        top_p = (0.5, 0.8, 0.9, 0.95)[j % 4]
+        st, tree, tokens = _tree_and_tokens(m, choices, cfg.K, cfg.topk, cfg.B, cfg.V, seed=seed)
+        logits = gen_verif_logits(cfg, st["parent"], tokens, seed=seed)
+        res = oracle.evaluate_posterior(logits, cfg.dtype, tokens, st, float(np.float32(0.7)),
+                                        top_p=float(np.float32(top_p)), sampling="nucleus")
+        say("nucleus seed sweep", cfg.name, seed, top_p)
+        banded += _check(st, res, logits, cfg.dtype,
+                         run_posterior(m, tree, logits, tokens, 0.7, top_p, "nucleus"))
+        decisions += cfg.B * (st["T"] - 1)
+    print(f"{cfg.name}: {nseeds} seeds, banded {banded} of {decisions} decisions")
+    assert banded <= max(2, decisions // 500)
