@@ -65,6 +65,8 @@ struct AttnPlan {
   int qtiles;     // work-group query tiles per (b, kv head)
   int splits;     // KV splits per (b, kv head, q tile)
   int nmb;        // 16-row blocks per wave of the bf16 kernel (1: 8 waves, 2: 4 waves)
+  int xrem;       // query tiles that also own one row past the last full 128-row tile (0: none)
+  int mpad;       // row stride of the split partials per (b, kv head)
   size_t ws_o, ws_ml, total;
 };
 AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_prefix_len);

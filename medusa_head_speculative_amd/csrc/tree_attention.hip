@@ -52,6 +52,7 @@ struct AttnArgs {
   float2* ml_part;   // [splits][B][Hkv][Mpad]
   long lcap;
   int B, Hq, Hkv, T, W, G, M, Mpad, qtiles, splits, nwork, Lmax;
+  int xrem, xbase;   // query tiles qt < xrem also own row xbase + qt (the extra-row kernel)
   float sl2;         // scale * log2(e)
   const float* rope_cs;  // [B*T][2][D/2] cos, sin of every node; queries are rotated when ROPE is set
 };
@@ -72,6 +73,18 @@ __device__ __forceinline__ bf16x8_t lds_read16(const uint16_t* p) {
 __device__ __forceinline__ s16x4_t lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4_t*)(p));
+}
+
+// A lane's value after a DPP move (quad permutation or a rotation inside the 16-lane row)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// c + a.lo * b.lo + a.hi * b.hi over two bf16 pairs (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
 // LDS tile layout: 64 K (or V) rows of D bf16, rows back to back; the 16-byte chunks of a row are
@@ -171,17 +184,35 @@ __device__ __forceinline__ void issue_mask(const uint64_t* __restrict__ mask, in
   }
 }
 
+// The extra row's mask word of one tree tile, into LDS by two lanes of wave 0
+__device__ __forceinline__ void issue_xmask(const uint64_t* __restrict__ mask, int W, int tt, int node,
+                                            uint64_t* Md, int wave, int lane) {
+  if (wave == 0 && lane < 2) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(mask + static_cast<long>(node) * W + tt) + lane;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)Md, 4, 0, 0);
+  }
+}
+
 // NMB 16-row blocks per wave and NW waves, so a work-group owns ROWS = NW * 16 * NMB query rows:
 // 128 with NW = 8 / NMB (NMB = 2 keeps more rows per wave, NMB = 1 twice the waves with half the
 // registers each, so four waves share a SIMD), or 144 with nine waves of one block, when a
 // (sequence, kv head) has a few rows past a multiple of 128 that would otherwise take a query
 // tile of their own and stream the whole K/V range once more.
-template <int D, bool ROPE, int NMB, int NW>
+// XR (4 waves of 32 rows): query tiles qt < xrem also own row xbase + qt, one row past the full
+// 128-row tiles, on the vector units.  In every K/V tile wave w takes keys 16w..16w+15 of that
+// row: a lane holds one key and a quarter of the head dim for the scores (bf16 pair dot products,
+// summed over the four quarters with row rotations that leave every copy with the same bits), and
+// for P V the transposed V reads of the matrix-core path give it four keys of one output column.
+// Each wave keeps its own online softmax state of the row; the four are merged at the end, in
+// wave order.  A lone row thus costs a few dozen vector instructions per tile and wave instead of
+// a sixteen-row block of matrix products, and the 4-wave form keeps two work-groups per CU.
+template <int D, bool ROPE, int NMB, int NW, bool XR = false>
 __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int RPW = NMB * 16;          // query rows per wave
   constexpr int ROWS = NW * RPW;         // query rows per work-group
   static_assert(ROWS == kAttnRows || ROWS == kAttnRowsWide, "a work-group owns 128 or 144 rows");
+  static_assert(!XR || (NMB == 2 && NW == 4), "the extra row is split over four waves of 16 keys");
   constexpr int NKB = D / 32;            // 32-wide contraction blocks over the head dim
   constexpr int NDB = D / 16;            // 16-wide output blocks over the head dim
   constexpr int TILE = kKvTile * D;      // elements per K (or V) tile
@@ -190,7 +221,10 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
   __shared__ __align__(16) uint16_t K1[TILE];
   __shared__ __align__(16) uint16_t V1[TILE];
   __shared__ int s_active[64];
-  __shared__ __align__(16) uint64_t s_mask[2][ROWS];   // mask words of the tree tile in flight
+  // mask words of the tree tile in flight (the extra row's last)
+  __shared__ __align__(16) uint64_t s_mask[2][ROWS + (XR ? 1 : 0)];
+  __shared__ float s_xo[XR ? NW : 1][XR ? D : 1];   // per-wave extra-row states for the merge
+  __shared__ float2 s_xml[XR ? NW : 1];
 
   // ---- work item; consecutive logical items (query tiles of one K/V range) share an XCD ----
   const int per_xcd = gridDim.x >> 3;
@@ -216,6 +250,10 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
   const int t_begin = static_cast<int>((static_cast<long>(split) * ntiles + a.splits - 1) / a.splits);
   const int t_end = static_cast<int>((static_cast<long>(split + 1) * ntiles + a.splits - 1) / a.splits);
   const long kvbase = (static_cast<long>(b) * a.Hkv + kvh) * a.lcap;
+  // the extra row of this query tile (XR), if it has one
+  const bool has_x = XR && qt < a.xrem;
+  const int xrow_m = has_x ? a.xbase + qt : 0;
+  const int xnode = xrow_m / a.G;
 
   // ---- tree tiles that some row of this work-group can see (only needed if the K/V range of
   //      this work-group reaches the tree rows) ----
@@ -242,6 +280,9 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
       for (int u = 0; u < 4; ++u)
         if (ok[u] && w[u] != 0ull) s_active[tt[u]] = 1;
     }
+    if (has_x)
+      for (int p = tid; p < ntt; p += NT)
+        if (a.mask[static_cast<long>(xnode) * a.W + p] != 0ull) s_active[p] = 1;
     __syncthreads();
   }
   auto next_active = [&](int t) {   // (uniform: every thread reads the same flags)
@@ -260,8 +301,9 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
 
   // node whose mask word this lane stages: row wave*RPW + lane/2 of the work-group
   const int mrow_m = qt * ROWS + wave * RPW + (lane >> 1);
-  // a wave whose rows are all past M only helps stage tiles and meets the barriers
-  const bool wave_active = qt * ROWS + wave * RPW < a.M;
+  // a wave whose rows are all past M only helps stage tiles and meets the barriers (the
+  // extra-row kernel runs only full 128-row tiles)
+  const bool wave_active = XR || qt * ROWS + wave * RPW < a.M;
   const int mrow_node = mrow_m < a.M ? mrow_m / a.G : 0;
 
   int voff[TileLoad<D, NW>::INST];   // this lane's byte offsets inside a tile
@@ -273,7 +315,10 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
     int nvalid;
     tile_rows(t, row0, nvalid);
     issue_tile<D, NW>(a.kc, a.vc, kvbase + row0, nvalid, K0, V0, wave, voff);
-    if (t >= np) issue_mask<RPW>(a.mask, a.W, t - np, mrow_node, s_mask[0], wave, lane);
+    if (t >= np) {
+      issue_mask<RPW>(a.mask, a.W, t - np, mrow_node, s_mask[0], wave, lane);
+      if (has_x) issue_xmask(a.mask, a.W, t - np, xnode, &s_mask[0][ROWS], wave, lane);
+    }
   }
 
   // ---- this lane's query rows (one per row block mb) ----
@@ -326,6 +371,52 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
     }
   }
 
+  // ---- the extra row: this lane's key of every tile and quarter of the head dim ----
+  constexpr int XCH = D / 32;                   // 16-byte chunks per lane
+  const int xkey = 16 * wave + 4 * lg + (mm & 3);
+  int xoff[XR ? XCH : 1];                       // element offsets of those chunks inside a tile
+  uint32_t qx[XR ? D / 8 : 1];                  // the query's bf16 pairs of the same chunks
+  float xo[XR ? NDB : 1];                       // P V partial of output column db*16 + mm
+  float xref = -INFINITY, xl = 0.f;             // reference (log2 domain) and row sum, per wave
+  if constexpr (XR) {
+    const int hqx = kvh * a.G + xrow_m % a.G;
+    const uint16_t* qrow = a.q + ((static_cast<long>(b) * a.Hq + hqx) * a.T + xnode) * D;
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      // the chunk order is rotated by the key so that the 16 lanes of one LDS pass read 16
+      // different bank groups
+      const int c = XCH * (mm >> 2) + (i ^ (mm & 3 & (XCH - 1)));
+      xoff[i] = tile_elem<D>(xkey, c);
+      uint4 v = has_x ? *reinterpret_cast<const uint4*>(qrow + c * 8) : make_uint4(0, 0, 0, 0);
+      if constexpr (ROPE) {
+        if (has_x) {
+          // rotate against the partner half of the head dim, as the other rows are rotated
+          constexpr int HC = D / 16;   // chunks per half
+          const uint4 pv = *reinterpret_cast<const uint4*>(qrow + (c ^ HC) * 8);
+          const float* cs = a.rope_cs + (static_cast<long>(b) * a.T + xnode) * D + (c & (HC - 1)) * 8;
+          uint32_t* ow = reinterpret_cast<uint32_t*>(&v);
+          const uint32_t* pw = reinterpret_cast<const uint32_t*>(&pv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int sh = 16 * (e & 1);
+            const float own = bf16_to_f32(static_cast<uint16_t>(ow[e >> 1] >> sh));
+            const float par = bf16_to_f32(static_cast<uint16_t>(pw[e >> 1] >> sh));
+            float x = c < HC ? own : par, y = c < HC ? par : own;
+            rope_rotate(cs[e], cs[D / 2 + e], x, y);
+            const float r = c < HC ? x : y;
+            ow[e >> 1] = (ow[e >> 1] & (0xffff0000u >> sh)) | (static_cast<uint32_t>(f32_to_bf16_rne(r)) << sh);
+          }
+        }
+      }
+      qx[4 * i] = v.x;
+      qx[4 * i + 1] = v.y;
+      qx[4 * i + 2] = v.z;
+      qx[4 * i + 3] = v.w;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) xo[db] = 0.f;
+  }
+
   float mrow[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) mrow[mb] = -INFINITY;
@@ -360,13 +451,17 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) mw[mb] &= s_mask[buf][wave * RPW + mb * 16 + mm];
     }
+    const uint64_t xmw = !has_x ? 0ull : is_tree ? (s_mask[buf][XR ? ROWS : 0] & vmask) : vmask;
     const int tn = next_active(t + 1);
     if (tn < t_end) {
       long nrow0;
       int nnvalid;
       tile_rows(tn, nrow0, nnvalid);
       issue_tile<D, NW>(a.kc, a.vc, kvbase + nrow0, nnvalid, Kn, Vn, wave, voff);
-      if (tn >= np) issue_mask<RPW>(a.mask, a.W, tn - np, mrow_node, s_mask[buf ^ 1], wave, lane);
+      if (tn >= np) {
+        issue_mask<RPW>(a.mask, a.W, tn - np, mrow_node, s_mask[buf ^ 1], wave, lane);
+        if (has_x) issue_xmask(a.mask, a.W, tn - np, xnode, &s_mask[buf ^ 1][ROWS], wave, lane);
+      }
     }
     if (!wave_active) {
       t = tn;
@@ -390,6 +485,23 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) sacc[mb][cb] = mfma16x16x32(kf, qf[mb][kb], sacc[mb][cb]);
       }
+    }
+    // the extra row's score of this lane's key, summed over the four quarters of the head dim
+    // by rotations of 8 and then 4 inside the 16-lane row (commutative pairs: equal bits)
+    float xs = 0.f;
+    if constexpr (XR) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < XCH; ++i) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(Kc + xoff[i]);
+        s0 = dot2_bf16(kv.x, qx[4 * i], s0);
+        s1 = dot2_bf16(kv.y, qx[4 * i + 1], s1);
+        s0 = dot2_bf16(kv.z, qx[4 * i + 2], s0);
+        s1 = dot2_bf16(kv.w, qx[4 * i + 3], s1);
+      }
+      xs = s0 + s1;
+      xs += dpp_f32<0x128>(xs);
+      xs += dpp_f32<0x124>(xs);
     }
 
     // ---- mask, online softmax (log2 domain), P as the B operand of the second product.
@@ -451,6 +563,29 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
       }
     }
 
+    // ---- the extra row's online softmax over this wave's 16 keys ----
+    uint32_t xp01 = 0u, xp23 = 0u;   // P of keys 4*lg + 0..3 of the wave's 16, as bf16 pairs
+    if constexpr (XR) {
+      xs = ((xmw >> xkey) & 1ull) ? xs : -INFINITY;
+      float mx = fmaxf(xs, dpp_f32<0xB1>(xs));   // quad_perm [1,0,3,2]
+      mx = fmaxf(mx, dpp_f32<0x4E>(mx));         // quad_perm [2,3,0,1]
+      mx = xor32_max(xor16_max(mx));
+      const float mxs = mx * a.sl2;
+      if (mxs > xref + 8.f) {
+        const float alpha = exp2f(xref - mxs);
+        xref = mxs;
+        xl *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) xo[db] *= alpha;
+      }
+      const float nm = xref == -INFINITY ? 0.f : -xref;
+      const float p = __builtin_amdgcn_exp2f(fmaf(xs, a.sl2, nm));
+      xp01 = pack_bf16x2(dpp_f32<0x00>(p), dpp_f32<0x55>(p));
+      xp23 = pack_bf16x2(dpp_f32<0xAA>(p), dpp_f32<0xFF>(p));
+      // row sum of the same bf16 values that weight V
+      xl = dot2_bf16(xp23, 0x3F803F80u, dot2_bf16(xp01, 0x3F803F80u, xl));
+    }
+
     // ---- O^T += V^T P^T; contraction index 8*lg+e <-> tile column
     //      ks*32 + (e < 4 ? 4*lg + e : 16 + 4*lg + e - 4), matching the score layout ----
     int vb_base = v_frag_base<D>(lg, mm);
@@ -480,6 +615,16 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
         lacc[mb] = mfma16x16x32(ones, __builtin_bit_cast(bf16x8_t, bv), lacc[mb]);
       }
     }
+    if constexpr (XR) {
+      // the transposed V read of this wave's 16 keys: columns 4*lg + 0..3 of output column
+      // db*16 + mm, the same layout as the matrix-core operand
+      const int xv = vb_base + (wave >> 1) * 32 * D + (wave & 1) * 16 * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint2 w = __builtin_bit_cast(uint2, lds_read_tr(Vc + (xv ^ (db << 4))));
+        xo[db] = dot2_bf16(w.y, xp23, dot2_bf16(w.x, xp01, xo[db]));
+      }
+    }
     t = tn;
     buf ^= 1;
   };
@@ -490,6 +635,39 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
     step(K0, V0, K1, V1);
     if (t >= t_end) break;
     step(K1, V1, K0, V0);
+  }
+
+  if constexpr (XR) {
+    // ---- the extra row: each wave's 16-key state, then the merge in wave order ----
+    const float lw = xor32_sum(xor16_sum(xl));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const float v = xor32_sum(xor16_sum(xo[db]));
+      if (lg == 0) s_xo[wave][db * 16 + mm] = v;
+    }
+    if (lane == 0) s_xml[wave] = make_float2(xref, lw);
+    __syncthreads();
+    if (has_x && tid < D) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_xml[w].x);
+      const float mu = mx == -INFINITY ? 0.f : mx;
+      float o = 0.f, l = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = exp2f(s_xml[w].x - mu);
+        o += s_xo[w][tid] * f;
+        l += s_xml[w].y * f;
+      }
+      if (a.splits == 1) {
+        const int hq = kvh * a.G + xrow_m % a.G;
+        a.out[((static_cast<long>(b) * a.Hq + hq) * a.T + xnode) * D + tid] = f32_to_bf16_rne(o * (1.f / l));
+      } else {
+        const long pr = ((static_cast<long>(split) * a.B + b) * a.Hkv + kvh) * a.Mpad + xrow_m;
+        a.o_part[pr * D + tid] = o;
+        if (tid == 0) a.ml_part[pr] = make_float2(mx, l);
+      }
+    }
   }
 
   // ---- finish: full row sums, then the output or this split's partial ----
@@ -713,15 +891,29 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
     // attention kernel gained 1 us and the merge of 16 splits instead of 10 lost 2.  Setting
     // MEDUSA_ATTN_ROWS to 128 or 144 forces the choice where it is possible.
     static const int forced_rows = [] { const char* v = getenv("MEDUSA_ATTN_ROWS"); return v ? atoi(v) : 0; }();
+    // extra rows on the vector units: -1 (unset) where the grid needs no split, 0 never, 1
+    // wherever the rows fit
+    static const int xrow_mode = [] { const char* v = getenv("MEDUSA_ATTN_XROW"); return v ? atoi(v) : -1; }();
     static const long target = wg_target_from_env();
-    const int q144 = (p.M + kAttnRowsWide - 1) / kAttnRowsWide;
-    const bool small_grid = static_cast<long>(B) * Hkv * p.qtiles < kAttnTwoBlockUnits;
-    const bool unsplit = static_cast<long>(B) * Hkv * q144 >= target;
-    const bool wide = forced_rows == kAttnRowsWide ? small_grid
-                    : forced_rows == kAttnRows ? false : small_grid && unsplit && q144 < p.qtiles;
-    if (wide) {
-      p.rows = kAttnRowsWide;
-      p.qtiles = q144;
+    // rows past the full 128-row tiles, one per tile at most: the 4-wave kernel takes them as
+    // extra rows instead of a query tile of their own
+    const int q128 = p.M / kAttnRows, rem = p.M - q128 * kAttnRows;
+    const bool x_fits = q128 >= 1 && rem >= 1 && rem <= q128;
+    const bool x_use = x_fits && (xrow_mode == 1 || (xrow_mode != 0 && forced_rows == 0 &&
+                                                     static_cast<long>(B) * Hkv * q128 >= target));
+    if (x_use) {
+      p.qtiles = q128;
+      p.xrem = rem;
+    } else {
+      const int q144 = (p.M + kAttnRowsWide - 1) / kAttnRowsWide;
+      const bool small_grid = static_cast<long>(B) * Hkv * p.qtiles < kAttnTwoBlockUnits;
+      const bool unsplit = static_cast<long>(B) * Hkv * q144 >= target;
+      const bool wide = forced_rows == kAttnRowsWide ? small_grid
+                      : forced_rows == kAttnRows ? false : small_grid && unsplit && q144 < p.qtiles;
+      if (wide) {
+        p.rows = kAttnRowsWide;
+        p.qtiles = q144;
+      }
     }
     const long units = static_cast<long>(B) * Hkv * p.qtiles;
     const int ntiles = (max_prefix_len + kKvTile - 1) / kKvTile + (T + kKvTile - 1) / kKvTile;
@@ -735,10 +927,12 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
       p.splits = s < 1 ? 1 : static_cast<int>(s);
     }
   }
-  p.nmb = p.rows == kAttnRows && static_cast<long>(B) * Hkv * p.qtiles * p.splits >= kAttnTwoBlockUnits ? 2 : 1;
+  p.nmb = p.xrem > 0 || (p.rows == kAttnRows &&
+                         static_cast<long>(B) * Hkv * p.qtiles * p.splits >= kAttnTwoBlockUnits) ? 2 : 1;
+  p.mpad = p.xrem > 0 ? p.M : p.qtiles * p.rows;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
-  const size_t rows = static_cast<size_t>(p.splits) * B * Hkv * p.qtiles * p.rows;
+  const size_t rows = static_cast<size_t>(p.splits) * B * Hkv * p.mpad;
   p.ws_o = take(p.splits > 1 ? rows * D * sizeof(float) : 0);
   p.ws_ml = take(p.splits > 1 ? rows * sizeof(float2) : 0);
   p.total = off;
@@ -784,7 +978,9 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
   a.W = W;
   a.G = P.G;
   a.M = P.M;
-  a.Mpad = P.qtiles * P.rows;
+  a.Mpad = P.mpad;
+  a.xrem = P.xrem;
+  a.xbase = P.qtiles * kAttnRows;
   a.qtiles = P.qtiles;
   a.splits = P.splits;
   a.nwork = B * Hkv * P.qtiles * P.splits;
@@ -793,20 +989,22 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc, 
   a.rope_cs = rope_cs;
   const unsigned grid = static_cast<unsigned>(((a.nwork + 7) / 8) * 8);
   hook_before(K_ATTENTION, s);
-#define MEDUSA_ATTN_LAUNCH(NMB_, NW_)                                                        \
+#define MEDUSA_ATTN_LAUNCH(NMB_, NW_, XR_)                                                   \
   if (rope_cs) {                                                                          \
-    if (D == 128) tree_attn_bf16<128, true, NMB_, NW_><<<grid, NW_ * 64, 0, s>>>(a);      \
-    else tree_attn_bf16<64, true, NMB_, NW_><<<grid, NW_ * 64, 0, s>>>(a);                \
+    if (D == 128) tree_attn_bf16<128, true, NMB_, NW_, XR_><<<grid, NW_ * 64, 0, s>>>(a);  \
+    else tree_attn_bf16<64, true, NMB_, NW_, XR_><<<grid, NW_ * 64, 0, s>>>(a);            \
   } else {                                                                                \
-    if (D == 128) tree_attn_bf16<128, false, NMB_, NW_><<<grid, NW_ * 64, 0, s>>>(a);     \
-    else tree_attn_bf16<64, false, NMB_, NW_><<<grid, NW_ * 64, 0, s>>>(a);               \
+    if (D == 128) tree_attn_bf16<128, false, NMB_, NW_, XR_><<<grid, NW_ * 64, 0, s>>>(a); \
+    else tree_attn_bf16<64, false, NMB_, NW_, XR_><<<grid, NW_ * 64, 0, s>>>(a);           \
   }
-  if (P.rows == kAttnRowsWide) {
-    MEDUSA_ATTN_LAUNCH(1, 9)
+  if (P.xrem > 0) {
+    MEDUSA_ATTN_LAUNCH(2, 4, true)
+  } else if (P.rows == kAttnRowsWide) {
+    MEDUSA_ATTN_LAUNCH(1, 9, false)
   } else if (P.nmb == 1) {
-    MEDUSA_ATTN_LAUNCH(1, 8)
+    MEDUSA_ATTN_LAUNCH(1, 8, false)
   } else {
-    MEDUSA_ATTN_LAUNCH(2, 4)
+    MEDUSA_ATTN_LAUNCH(2, 4, false)
   }
 #undef MEDUSA_ATTN_LAUNCH
   hook_after(K_ATTENTION, s);

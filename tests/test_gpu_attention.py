@@ -77,9 +77,14 @@ CASES = [
     ("bf16", 3, 64, 8, 128, "c4", [3, 40, 64]),
     ("bf16", 3, 64, 8, 64, "c4", [0, 17, 65]),
     ("bf16", 2, 4, 4, 128, "one", [0, 3]),
-    # 129 and 130 query rows per kv head with 256 (sequence, kv head) pairs: one 144-row
-    # work-group of nine waves each, instead of a 128-row tile and a 1- or 2-row one
+    # 129 query rows per kv head with at least 256 (sequence, kv head) pairs: a 128-row tile of
+    # the 4-wave kernel with the 129th row on the vector units (keys split over the waves)
     ("bf16", 2, 128, 128, 128, "c3", [64, 200]),
+    ("bf16", 2, 128, 128, 128, "c3", [0, 1]),
+    ("bf16", 2, 128, 128, 64, "c3", [63, 130]),
+    ("bf16", 4, 192, 64, 128, "cart2x20", [5, 190, 0, 64]),   # 3 q heads x 43 nodes: (node 42, head 2)
+    ("bf16", 1, 128, 128, 128, "cart16x15", [70]),      # 257 rows: only the first tile has one
+    # 130 rows per kv head (two past the tile): one 144-row work-group of nine waves each
     ("bf16", 4, 128, 64, 64, "c1", [0, 1, 100, 63]),
     ("f32", 2, 4, 2, 64, "c1", [0, 77]),
     ("f32", 1, 2, 2, 128, "c0", [1]),
@@ -90,6 +95,10 @@ CASES = [
 def _choices(name):
     if name == "chain8":
         return cartesian_choices([1] * 8), 1, 8
+    if name == "cart2x20":
+        return cartesian_choices([2, 20]), 20, 2
+    if name == "cart16x15":
+        return cartesian_choices([16, 15]), 16, 2
     if name == "one":
         return [[0]], 1, 1
     return load_tree_choices(name), 10, 5
@@ -128,4 +137,15 @@ def test_attention_deterministic():
     say("attention determinism")
     o1 = run_attn(m, a, mask_array(st), 8)
     o2 = run_attn(m, a, mask_array(st), 8)
+    assert np.array_equal(o1, o2)
+
+
+def test_attention_extra_row_deterministic():
+    m = lib()
+    cfg = custom(dtype="bf16", B=2, Hq=128, Hkv=128, D=128, L=300, seed=5)
+    st = oracle.build_static(load_tree_choices("c3"), 10, 5)
+    a = gen_attention_inputs(cfg, st["T"])
+    say("attention determinism, extra-row kernel")
+    o1 = run_attn(m, a, mask_array(st), 128)
+    o2 = run_attn(m, a, mask_array(st), 128)
     assert np.array_equal(o1, o2)
