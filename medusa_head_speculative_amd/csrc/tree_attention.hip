@@ -154,21 +154,31 @@ __device__ __forceinline__ void tile_voffsets(int wave, int lane, int (&voff)[Ti
   }
 }
 
+// stream: nontemporal loads (each K/V row is read by this work-group only)
 template <int D, int NW>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kc,
                                            const uint16_t* __restrict__ vc, long rowbase,
                                            int nvalid, uint16_t* Kd, uint16_t* Vd, int wave,
-                                           const int* voff) {
+                                           const int* voff, bool stream = false) {
   using TL = TileLoad<D, NW>;
   if (NW > TL::NWL && wave >= TL::NWL) return;
   const int bytes = nvalid * D * 2;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + rowbase * D), 0, bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + rowbase * D), 0, bytes, 0x00020000);
+  if (stream) {
 #pragma unroll
-  for (int u = 0; u < TL::INST; ++u) {
-    const int rbase = (wave * TL::INST + u) * TL::RPI;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Kd + rbase * D), 16, voff[u], 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vd + rbase * D), 16, voff[u], 0, 0, 0);
+    for (int u = 0; u < TL::INST; ++u) {
+      const int rbase = (wave * TL::INST + u) * TL::RPI;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Kd + rbase * D), 16, voff[u], 0, 0, 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vd + rbase * D), 16, voff[u], 0, 0, 2);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < TL::INST; ++u) {
+      const int rbase = (wave * TL::INST + u) * TL::RPI;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Kd + rbase * D), 16, voff[u], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vd + rbase * D), 16, voff[u], 0, 0, 0);
+    }
   }
 }
 
@@ -308,13 +318,17 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
 
   int voff[TileLoad<D, NW>::INST];   // this lane's byte offsets inside a tile
   tile_voffsets<D, NW>(wave, lane, voff);
+  // With one query tile per (sequence, kv head) no other work-group reads these K/V rows: the
+  // extra-row kernel then streams them with nontemporal loads (on the 33B shape attention went
+  // from 106 to 101.5 us; the split grids of the other forms measured no gain or a loss).
+  const bool stream = XR && a.qtiles == 1;
   int t = next_active(t_begin);
   int buf = 0;
   if (t < t_end) {
     long row0;
     int nvalid;
     tile_rows(t, row0, nvalid);
-    issue_tile<D, NW>(a.kc, a.vc, kvbase + row0, nvalid, K0, V0, wave, voff);
+    issue_tile<D, NW>(a.kc, a.vc, kvbase + row0, nvalid, K0, V0, wave, voff, stream);
     if (t >= np) {
       issue_mask<RPW>(a.mask, a.W, t - np, mrow_node, s_mask[0], wave, lane);
       if (has_x) issue_xmask(a.mask, a.W, t - np, xnode, &s_mask[0][ROWS], wave, lane);
@@ -378,7 +392,13 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
   uint32_t qx[XR ? D / 8 : 1];                  // the query's bf16 pairs of the same chunks
   float xo[XR ? NDB : 1];                       // P V partial of output column db*16 + mm
   float xref = -INFINITY, xl = 0.f;             // reference (log2 domain) and row sum, per wave
+  int xva[XR ? NDB : 1];                        // byte offsets of its transposed V reads
   if constexpr (XR) {
+    // this wave's 16 keys: rows 16*wave.. of the tile, the block the matrix-core path reads as
+    // (ks, hi) = (wave / 2, wave % 2)
+    const int xv = v_frag_base<D>(lg, mm) + (wave >> 1) * 32 * D + (wave & 1) * 16 * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) xva[db] = (xv ^ (db << 4)) * 2;
     const int hqx = kvh * a.G + xrow_m % a.G;
     const uint16_t* qrow = a.q + ((static_cast<long>(b) * a.Hq + hqx) * a.T + xnode) * D;
 #pragma unroll
@@ -451,13 +471,19 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) mw[mb] &= s_mask[buf][wave * RPW + mb * 16 + mm];
     }
-    const uint64_t xmw = !has_x ? 0ull : is_tree ? (s_mask[buf][XR ? ROWS : 0] & vmask) : vmask;
+    // the extra row's visible keys: those below xlim that its mask word (tree tiles) selects
+    uint64_t xw = 0ull;
+    int xlim = 0;
+    if constexpr (XR) {
+      xw = is_tree ? s_mask[buf][ROWS] : ~0ull;
+      xlim = has_x ? nvalid : 0;
+    }
     const int tn = next_active(t + 1);
     if (tn < t_end) {
       long nrow0;
       int nnvalid;
       tile_rows(tn, nrow0, nnvalid);
-      issue_tile<D, NW>(a.kc, a.vc, kvbase + nrow0, nnvalid, Kn, Vn, wave, voff);
+      issue_tile<D, NW>(a.kc, a.vc, kvbase + nrow0, nnvalid, Kn, Vn, wave, voff, stream);
       if (tn >= np) {
         issue_mask<RPW>(a.mask, a.W, tn - np, mrow_node, s_mask[buf ^ 1], wave, lane);
         if (has_x) issue_xmask(a.mask, a.W, tn - np, xnode, &s_mask[buf ^ 1][ROWS], wave, lane);
@@ -532,17 +558,22 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sv[cb][j]);
-      mx = xor32_max(xor16_max(mx));
-      const float mxs = mx * a.sl2;
-      if (mxs > mrow[mb] + 8.f) {                     // raise the reference (rare after the start)
-        const float alpha = exp2f(mrow[mb] - mxs);
-        mrow[mb] = mxs;
+      // A row's maximum exceeds its reference + 8 only if the maximum of one of its four lanes
+      // does (scaling is monotonic), so the cross-lane maximum is taken only when some lane of
+      // the wave sees such a column: rare after the first tiles.
+      if (__builtin_amdgcn_ballot_w64(mx * a.sl2 > mrow[mb] + 8.f) != 0ull) {
+        mx = xor32_max(xor16_max(mx));
+        const float mxs = mx * a.sl2;
+        if (mxs > mrow[mb] + 8.f) {                   // raise the reference
+          const float alpha = exp2f(mrow[mb] - mxs);
+          mrow[mb] = mxs;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lacc[mb][j] *= alpha;
+          for (int j = 0; j < 4; ++j) lacc[mb][j] *= alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) oacc[mb][db][j] *= alpha;
+            for (int j = 0; j < 4; ++j) oacc[mb][db][j] *= alpha;
+        }
       }
       const float nm = mrow[mb] == -INFINITY ? 0.f : -mrow[mb];
       float pr[4][4];
@@ -566,12 +597,13 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
     // ---- the extra row's online softmax over this wave's 16 keys ----
     uint32_t xp01 = 0u, xp23 = 0u;   // P of keys 4*lg + 0..3 of the wave's 16, as bf16 pairs
     if constexpr (XR) {
-      xs = ((xmw >> xkey) & 1ull) ? xs : -INFINITY;
-      float mx = fmaxf(xs, dpp_f32<0xB1>(xs));   // quad_perm [1,0,3,2]
-      mx = fmaxf(mx, dpp_f32<0x4E>(mx));         // quad_perm [2,3,0,1]
-      mx = xor32_max(xor16_max(mx));
-      const float mxs = mx * a.sl2;
-      if (mxs > xref + 8.f) {
+      xs = (xkey < xlim && ((xw >> xkey) & 1ull)) ? xs : -INFINITY;
+      // the reference (one per wave) is raised when some key of the wave's 16 passes it by 8
+      if (__builtin_amdgcn_ballot_w64(xs * a.sl2 > xref + 8.f) != 0ull) {
+        float mx = fmaxf(xs, dpp_f32<0xB1>(xs));   // quad_perm [1,0,3,2]
+        mx = fmaxf(mx, dpp_f32<0x4E>(mx));         // quad_perm [2,3,0,1]
+        mx = xor32_max(xor16_max(mx));
+        const float mxs = mx * a.sl2;
         const float alpha = exp2f(xref - mxs);
         xref = mxs;
         xl *= alpha;
@@ -618,10 +650,10 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
     if constexpr (XR) {
       // the transposed V read of this wave's 16 keys: columns 4*lg + 0..3 of output column
       // db*16 + mm, the same layout as the matrix-core operand
-      const int xv = vb_base + (wave >> 1) * 32 * D + (wave & 1) * 16 * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint2 w = __builtin_bit_cast(uint2, lds_read_tr(Vc + (xv ^ (db << 4))));
+        const uint2 w = __builtin_bit_cast(uint2, lds_read_tr(reinterpret_cast<const uint16_t*>(
+                                                      reinterpret_cast<const char*>(Vc) + xva[db])));
         xo[db] = dot2_bf16(w.y, xp23, dot2_bf16(w.x, xp01, xo[db]));
       }
     }
