@@ -923,15 +923,18 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
     // attention kernel gained 1 us and the merge of 16 splits instead of 10 lost 2.  Setting
     // MEDUSA_ATTN_ROWS to 128 or 144 forces the choice where it is possible.
     static const int forced_rows = [] { const char* v = getenv("MEDUSA_ATTN_ROWS"); return v ? atoi(v) : 0; }();
-    // extra rows on the vector units: -1 (unset) where the grid needs no split, 0 never, 1
-    // wherever the rows fit
+    // extra rows on the vector units: -1 (unset) one or two where the grid needs no split, 0
+    // never, 1 wherever the rows fit
     static const int xrow_mode = [] { const char* v = getenv("MEDUSA_ATTN_XROW"); return v ? atoi(v) : -1; }();
     static const long target = wg_target_from_env();
     // rows past the full 128-row tiles, one per tile at most: the 4-wave kernel takes them as
-    // extra rows instead of a query tile of their own
+    // extra rows instead of a query tile of their own.  An extra row costs its work-group about a
+    // fifth of its time (70B-layer shape: 56 extra rows per kv head took 1.46-1.52 ms against
+    // 1.24-1.29 ms with a 56-row query tile), so by default only one or two rows are taken
+    // (33B shape: one row, 135 -> 103 us against the nine-wave 144-row form).
     const int q128 = p.M / kAttnRows, rem = p.M - q128 * kAttnRows;
     const bool x_fits = q128 >= 1 && rem >= 1 && rem <= q128;
-    const bool x_use = x_fits && (xrow_mode == 1 || (xrow_mode != 0 && forced_rows == 0 &&
+    const bool x_use = x_fits && (xrow_mode == 1 || (xrow_mode != 0 && forced_rows == 0 && rem <= 2 &&
                                                      static_cast<long>(B) * Hkv * q128 >= target));
     if (x_use) {
       p.qtiles = q128;
