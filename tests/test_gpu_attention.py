@@ -149,3 +149,57 @@ def test_attention_extra_row_deterministic():
     o1 = run_attn(m, a, mask_array(st), 128)
     o2 = run_attn(m, a, mask_array(st), 128)
     assert np.array_equal(o1, o2)
+
+
+def _random_tree_exact(rng, n, topk=8, max_depth=6):
+    """A random prefix-closed choice list of exactly n nodes (each new child takes its parent's
+    next free rank)."""
+    nodes, used = [()], {(): 0}
+    while len(nodes) < n + 1:
+        parent = nodes[int(rng.integers(len(nodes)))]
+        if len(parent) >= max_depth or used[parent] >= topk:
+            continue
+        child = parent + (used[parent],)
+        used[parent] += 1
+        used[child] = 0
+        nodes.append(child)
+    return [list(t) for t in nodes[1:]]
+
+
+# (G, T, B, Hkv, D): 128 * q + r rows per kv head, r in {1, 2}, with enough (sequence, kv head)
+# pairs that the plan takes the extra rows; with two query tiles only the first r own one
+XROW_CASES = [(1, 129, 2, 128, 128), (1, 129, 1, 256, 64), (1, 257, 1, 128, 128),
+              (1, 258, 1, 128, 64), (2, 129, 1, 128, 128), (1, 129, 4, 64, 128)]
+
+
+@pytest.mark.parametrize("i", range(len(XROW_CASES)))
+def test_attention_extra_row_random(i):
+    """Random trees and ragged prefixes on shapes the extra-row kernel takes; every output
+    against the float32 device reference, itself pinned to the oracle on sampled units."""
+    G, T, B, Hkv, D = XROW_CASES[i]
+    rng = rng_for(1300 + i, 0)
+    m = lib()
+    st = oracle.build_static(_random_tree_exact(rng, T - 1), 8, 6)
+    assert st["T"] == T
+    pls = [int(x) for x in rng.choice([0, 1, 63, 64, 65, 200], size=B)]
+    cfg = custom(dtype="bf16", B=B, Hq=G * Hkv, Hkv=Hkv, D=D, L=max(pls), seed=1300 + i)
+    a = gen_attention_inputs(cfg, T, prefix_lens=pls, lcap=max(pls) + T + 5)
+    nan = np.uint16(0x7FC0)
+    for b, L in enumerate(pls):
+        a["k_cache"][b, :, L + T:] = nan
+        a["v_cache"][b, :, L + T:] = nan
+    mask = mask_array(st)
+    say("attention extra row", dict(G=G, T=T, B=B, Hkv=Hkv, D=D, pls=pls))
+    out = as_f64(run_attn(m, a, mask, Hkv), "bf16")
+    assert not np.isnan(out).any()
+    sel = sample_units(B, G * Hkv, T, 200, 1300 + i)
+    ref = oracle.tree_attention(a["q"], a["k_cache"], a["v_cache"], "bf16", a["prefix_len"],
+                                st["mask"], Hkv, sel=sel)
+    ref = ref[sel[:, 0], sel[:, 1], sel[:, 2]]
+    every = attention_all_f32(a["q"], a["k_cache"], a["v_cache"], a["prefix_len"], mask, Hkv)
+    pin = float(np.abs(every[sel[:, 0], sel[:, 1], sel[:, 2]] - ref).max())
+    assert pin <= 1e-4, pin
+    assert float(np.abs(out[sel[:, 0], sel[:, 1], sel[:, 2]] - ref).max()) <= tol("bf16")
+    err = float(np.abs(out - every).max())
+    print(f"extra-row case {i}: max |out - f32 reference| = {err:.3e}, reference vs oracle {pin:.1e}")
+    assert err <= tol("bf16")
