@@ -15,9 +15,11 @@
 //                 V^T comes from LDS with ds_read_b64_tr_b16 (16-lane transposed reads), so V is
 //                 never transposed in memory.
 // Tree tiles that no row of the work-group can see are skipped; inside a tile each row's mask
-// word selects its ancestors.  When there are too few (sequence, kv head, query tile) units to
-// fill the chip, the K/V range is split and a second kernel merges the partial results in a
-// fixed order.  fp32 path (small models): one wave per output row, plain FMAs.
+// word selects its ancestors.  A row or two past the last full 128-row tile ride along as extra
+// rows on the vector units (bf16 pair dot products) instead of taking a query tile of their own.
+// When there are too few (sequence, kv head, query tile) units to fill the chip, the K/V range
+// is split and a second kernel merges the partial results in a fixed order.  fp32 path (small
+// models): one wave per output row, plain FMAs.
 #include <math.h>
 #include <stdlib.h>
 
@@ -33,10 +35,10 @@ constexpr int kMaxSplits = 16;
 // Work-groups at or above which the bf16 kernel keeps two row blocks per wave (4 waves of 32
 // rows, 204 VGPRs, two waves per SIMD) instead of one (8 waves of 16 rows, 118 VGPRs, four per
 // SIMD).  Measured on MI355X: the 8-wave form is faster on grids up to a few rounds of the 512
-// work-groups that fit at two per CU (c1 16.2 -> 15.1 us, c2 21.5 -> 20.0, c3 159 -> 155 at 832
-// work-groups), and no faster on the 70B-layer grid of 2240 (1277-1307 against 1293 us; its
-// rotary variant 1264-1283 against 1326-1329), where each wave reading K for only 16 rows
-// doubles the LDS traffic per row.
+// work-groups that fit at two per CU (7B shape 16.2 -> 15.1 us, Llama-8B shape 21.5 -> 20.0,
+// 33B shape 159 -> 155 at 832 work-groups), and no faster on the 70B-layer grid of 2240
+// (1277-1307 against 1293 us; its rotary variant 1264-1283 against 1326-1329), where each wave
+// reading K for only 16 rows doubles the LDS traffic per row.
 constexpr long kAttnTwoBlockUnits = 1536;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
