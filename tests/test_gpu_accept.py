@@ -79,11 +79,15 @@ def test_accept_full_size(ci, temp):
     (20001, "c4", 5, 0.7),      # 555 rows: 2 rounds per chunk, element loads (V % 8 != 0)
     (131072, "chain8", 16, 0.7),   # 128 rows: 4 rounds per chunk, vector loads
     (131077, "chain8", 16, 0.0),   # 4 rounds per chunk, element loads, ragged last chunk
+    (1000, "max4096", 2, 0.7),     # the largest tree: 4096 tokens, 64 internal rows, 4032 paths
+    (1000, "max4096", 2, 0.0),
 ])
 def test_accept_edges(dtype, V, tree, B, temp):
     m = lib()
     if tree == "one":
         choices, K, topk = [[0]], 1, 1
+    elif tree == "max4096":
+        choices, K, topk = cartesian_choices([63, 64]), 2, 64
     elif tree in ("chain6", "chain8"):
         depth = int(tree[5:])
         choices, K, topk = cartesian_choices([1] * depth), depth, 1

@@ -89,12 +89,17 @@ CASES = [
     ("f32", 2, 4, 2, 64, "c1", [0, 77]),
     ("f32", 1, 2, 2, 128, "c0", [1]),
     ("f32", 1, 8, 1, 64, "c3", [200]),
+    # the largest tree (4096 tokens, 64 tree tiles and mask words): 8192 rows per kv head
+    ("bf16", 1, 2, 1, 128, "max4096", [100]),
+    ("f32", 1, 2, 2, 64, "max4096", [5]),
 ]
 
 
 def _choices(name):
     if name == "chain8":
         return cartesian_choices([1] * 8), 1, 8
+    if name == "max4096":
+        return cartesian_choices([63, 64]), 64, 2
     if name == "cart2x20":
         return cartesian_choices([2, 20]), 20, 2
     if name == "cart16x15":

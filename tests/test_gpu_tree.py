@@ -58,6 +58,7 @@ def test_workload_trees(name, K):
     (cartesian_choices([64]), 1, 64),
     (cartesian_choices([3, 3, 3, 3]), 4, 3),
     (cartesian_choices([4, 4, 4, 4, 3]), 5, 4),   # T = 1365 + ... : 22 mask words
+    (cartesian_choices([63, 64]), 2, 64),          # T = 4096, the largest tree: 64 mask words
 ])
 def test_edge_trees(choices, K, topk):
     _check_tree(choices, K, topk, 3, seed=K * 11 + topk)
