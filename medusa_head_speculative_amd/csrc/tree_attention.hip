@@ -33,7 +33,7 @@ constexpr int kAttnRowsWide = 144;   // ... or 9 waves x 16 when that takes fewe
 constexpr int kKvTile = 64;
 constexpr int kMaxSplits = 16;
 // Work-groups at or above which the bf16 kernel keeps two row blocks per wave (4 waves of 32
-// rows, 204 VGPRs, two waves per SIMD) instead of one (8 waves of 16 rows, 118 VGPRs, four per
+// rows, 198 VGPRs, two waves per SIMD) instead of one (8 waves of 16 rows, 120 VGPRs, four per
 // SIMD).  Measured on MI355X: the 8-wave form is faster on grids up to a few rounds of the 512
 // work-groups that fit at two per CU (7B shape 16.2 -> 15.1 us, Llama-8B shape 21.5 -> 20.0,
 // 33B shape 159 -> 155 at 832 work-groups), and no faster on the 70B-layer grid of 2240
@@ -942,9 +942,10 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int T, int D, int max_pref
   if (dtype == 1) {
     // 144-row work-groups (nine waves of one row block) when they take fewer query tiles than
     // 128-row ones, leave enough work-groups that the K/V range needs no split, and keep the grid
-    // in the one-block-per-wave range.  At 118 VGPRs only one nine-wave work-group fits on a CU;
-    // still, on the 33B shape (129 rows per kv head: a 128-row tile and a 1-row tile that streams
-    // the whole K/V range again) attention went from 157.5 to 137.8 us.  Forcing two per CU
+    // in the one-block-per-wave range (and the extra rows below do not apply).  At 118-120
+    // VGPRs only one nine-wave work-group fits on a CU; still, on the 33B shape (129 rows per kv
+    // head: a 128-row tile and a 1-row tile that streams the whole K/V range again) attention
+    // went from 157.5 to 137.8 us.  Forcing two per CU
     // (five waves per SIMD: 96 VGPRs, 3 spilled, with the buffer-load tiles) took 138-140 us
     // against 135.5-136.2 on the same GPU.  On the Llama-8B shape (260 rows, split grid) the
     // attention kernel gained 1 us and the merge of 16 splits instead of 10 lost 2.  Setting
