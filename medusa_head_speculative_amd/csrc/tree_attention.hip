@@ -405,9 +405,10 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16(AttnArgs a) {
     const uint16_t* qrow = a.q + ((static_cast<long>(b) * a.Hq + hqx) * a.T + xnode) * D;
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-      // the chunk order is rotated by the key so that the 16 lanes of one LDS pass read 16
-      // different bank groups
-      const int c = XCH * (mm >> 2) + (i ^ (mm & 3 & (XCH - 1)));
+      // lanes of odd 16-lane rows take the chunks in pair-swapped order: the lanes that one LDS
+      // cycle serves then hit distinct bank groups (a probe of the bank-conflict counter read
+      // zero this way, and two-way conflicts for orders set by the key)
+      const int c = XCH * (mm >> 2) + (i ^ (lg & 1 & (XCH - 1)));
       xoff[i] = tile_elem<D>(xkey, c);
       uint4 v = has_x ? *reinterpret_cast<const uint4*>(qrow + c * 8) : make_uint4(0, 0, 0, 0);
       if constexpr (ROPE) {
