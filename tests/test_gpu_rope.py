@@ -115,3 +115,38 @@ def test_rope_attention_edges(dtype, D, B, Hq, Hkv, tree, pls, posmode):
     err = float(np.abs(as_f64(out, dtype) - ref).max())
     print(f"edge {dtype} D{D} {tree}: max err {err:.3e}")
     assert err <= tol(dtype)
+
+
+@pytest.mark.parametrize("G,T,B,Hkv,D,base", [(1, 129, 2, 128, 128, 10000.0),
+                                              (2, 129, 1, 128, 64, 500000.0)])
+def test_rope_attention_extra_row(G, T, B, Hkv, D, base):
+    """Rotary attention on shapes the extra-row kernel takes (random trees, ragged prefixes):
+    the extra row's query is rotated in registers like the others.  Every output against the
+    float32 device reference over the oracle's rotated q and keys, pinned to the oracle."""
+    from test_gpu_attention import _random_tree_exact
+    from synth.gen import rng_for
+    m = lib()
+    rng = rng_for(1400 + G * 7 + D, 0)
+    st = oracle.build_static(_random_tree_exact(rng, T - 1), 8, 6)
+    pls = [int(x) for x in rng.choice([0, 1, 63, 64, 65, 200], size=B)]
+    cfg = custom(dtype="bf16", B=B, Hq=G * Hkv, Hkv=Hkv, D=D, L=max(pls), seed=1400 + D)
+    a = gen_attention_inputs(cfg, T, prefix_lens=pls)
+    pos = np.array([[pls[b] + d for d in st["depth"]] for b in range(B)], np.int32)
+    say("rope attention, extra row", dict(G=G, T=T, B=B, Hkv=Hkv, D=D, pls=pls))
+    out, kc = run_rope(m, a, mask_array(st), Hkv, pos, base)
+    qr, kr = oracle.rotate_tree(a["q"], a["k_cache"], "bf16", a["prefix_len"], pos, base)
+    check_keys(kc, kr, "bf16", T, a["prefix_len"])
+    rs = np.random.default_rng(1400 + G)
+    sel = np.stack([rs.integers(0, B, 300), rs.integers(0, G * Hkv, 300),
+                    np.full(300, T - 1)], 1).astype(np.int32)   # the last node: the extra row
+    ref = oracle.tree_attention(qr, kr, a["v_cache"], "bf16", a["prefix_len"], st["mask"], Hkv,
+                                sel=sel)[sel[:, 0], sel[:, 1], sel[:, 2]]
+    every = attention_all_f32(qr, kr, a["v_cache"], a["prefix_len"], mask_array(st), Hkv)
+    pin = float(np.abs(every[sel[:, 0], sel[:, 1], sel[:, 2]] - ref).max())
+    assert pin <= 1e-4, pin
+    got = as_f64(out, "bf16")
+    assert not np.isnan(got).any()
+    assert float(np.abs(got[sel[:, 0], sel[:, 1], sel[:, 2]] - ref).max()) <= tol("bf16")
+    err = float(np.abs(got - every).max())
+    print(f"rope extra row G={G} D={D}: max |out - f32 reference| = {err:.3e}")
+    assert err <= tol("bf16")
